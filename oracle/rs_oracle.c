@@ -1,0 +1,380 @@
+/*
+ * rs_oracle.c -- plain, slow, fp64 CPU oracle for the batched speculative-
+ * sampling verify step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark use it.  It shares no code, header, table or constant with the
+ * HIP library; its Philox4x32-10 is written here from the published
+ * definition.
+ *
+ * What it computes (citations name the page title and section):
+ *
+ *  - Target distribution: temperature softmax of the target logits,
+ *    p = softmax(l / T), applied to the target only.
+ *      [Ch.12 "投机解码：以小博大" §12.2.3; §12.9, compute_probs bullet]
+ *  - Accept test at each draft position j, in order: draw u ~ U[0,1) and
+ *    accept the draft token x* iff u * q(x*) < p(x*), which is the rule
+ *    "accept with probability min(1, p(x*)/q(x*))".
+ *      [Ch.12 §12.2.1 steps 1-3; "投机解码（Speculative Decoding）端到端深挖"
+ *       §7.3 path C (coin * q < p)]
+ *    With no draft probabilities the draft is deterministic and q is one-hot
+ *    at x*, so q(x*) = 1.  [Ch.12 §12.2.3; §12.9, last bullet]
+ *  - First-rejection prefix: drafts after the first rejected one are
+ *    discarded.  [Ch.12 §12.9, "one program per request checks its k drafts
+ *    in order"; "vllm v1 源码精读（五）" §7]
+ *  - At the first rejected position j = n < K: resample from the residual
+ *    max(0, p - q) / sum max(0, p - q)  [Ch.12 §12.2.1 step 3, §12.2.2];
+ *    with one-hot q this is p with p(x*) set to zero, renormalised
+ *    [Ch.12 §12.9, last bullet].
+ *  - If all K drafts are accepted, sample a bonus token from p at position K.
+ *    [Ch.12 §12.3.2; "投机解码深度实战" §一 item 4]
+ *  - Sampling is an exponential race: argmax_x r(x) / E_x with E_x ~ Exp(1),
+ *    which samples r / sum(r) without normalising it.
+ *      [Ch.12 §12.9, last bullet: argmax(prob / exponential)]
+ *  - Greedy requests (temperature <= 0, or the greedy entry point): accept
+ *    iff draft == argmax of the target logits; at the first mismatch, or as
+ *    the bonus, emit the target argmax.
+ *      [Ch.12 §12.2.4; §12.9 first bullet (temperature sentinel -1);
+ *       "投机解码端到端深挖" §7.1 path A]
+ *  - Output: the accepted drafts, then one target token; num_accepted = n,
+ *    so n + 1 tokens are emitted.  [Ch.12 §12.3.4; "投机解码端到端深挖"
+ *    §8 (accept_lens = num_correct_drafts + 1)]
+ *
+ * Readings where the pages leave a step open (each is also listed in the
+ * design notes):
+ *  - Random stream: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
+ *    Random Numbers: As Easy as 1, 2, 3", SC'11), key = 64-bit seed
+ *    (low word, high word), counter = (c0, j, b, tag).
+ *      accept uniform  u_j = (w0 >> 8) * 2^-24, counter (0, j, b, 0), word 0;
+ *      race exponential E_x = -ln U_x, U_x = ((w >> 9) + 1/2) * 2^-23,
+ *        counter (x >> 2, j, b, 1), word (x & 3).
+ *  - Greedy and race ties: lowest token index wins.
+ *  - All-zero residual after a rejection (possible only through rounding):
+ *    race over p at that position instead, and flag the request.
+ *  - Requests whose metadata is out of range (cu not within [0, D], K_b >
+ *    max_k, a draft id outside [0, V)) emit -1 everywhere and
+ *    num_accepted = -1.
+ *
+ * Near-tie flags (a request is flagged when a decision on its taken path
+ * would change under a relative perturbation eps of p and of E):
+ *   accept test:  |p(x*) - u q(x*)| <= eps * p(x*)
+ *   race:         lower bound of the winner's key <= upper bound of any
+ *                 other key, the bounds taken with p -> p(1 -/+ eps) and
+ *                 E -> E(1 +/- eps).
+ *
+ * Arithmetic: inputs are widened exactly (bf16 -> fp32 -> fp64; temperature
+ * from fp32) and everything is computed in fp64 with the C library's exp/log.
+ * Requests are independent; OpenMP runs them in parallel without changing
+ * any request's arithmetic.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define RSO_F32 0
+#define RSO_BF16 1
+
+#define RSO_FLAG_ACCEPT_TIE 1
+#define RSO_FLAG_RACE_TIE 2
+#define RSO_FLAG_ZERO_RESIDUAL 4
+#define RSO_FLAG_INVALID 8
+
+/* ------------------------------------------------------------------------ */
+/* Philox4x32-10.  One round maps (c0, c1, c2, c3) with key (k0, k1) to
+ *   (hi(M1*c2) ^ c1 ^ k0,  lo(M1*c2),  hi(M0*c0) ^ c3 ^ k1,  lo(M0*c0))
+ * and the key is advanced by the Weyl constants between rounds. */
+static const uint32_t PHILOX_M0 = 0xD2511F53u;
+static const uint32_t PHILOX_M1 = 0xCD9E8D57u;
+static const uint32_t PHILOX_W0 = 0x9E3779B9u;
+static const uint32_t PHILOX_W1 = 0xBB67AE85u;
+
+void rso_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4]) {
+  uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+  uint32_t k0 = key_in[0], k1 = key_in[1];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += PHILOX_W0;
+      k1 += PHILOX_W1;
+    }
+    uint64_t prod0 = (uint64_t)PHILOX_M0 * (uint64_t)c0;
+    uint64_t prod1 = (uint64_t)PHILOX_M1 * (uint64_t)c2;
+    uint32_t hi0 = (uint32_t)(prod0 >> 32), lo0 = (uint32_t)prod0;
+    uint32_t hi1 = (uint32_t)(prod1 >> 32), lo1 = (uint32_t)prod1;
+    uint32_t n0 = hi1 ^ c1 ^ k0;
+    uint32_t n1 = lo1;
+    uint32_t n2 = hi0 ^ c3 ^ k1;
+    uint32_t n3 = lo0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+static void seed_key(uint64_t seed, uint32_t key[2]) {
+  key[0] = (uint32_t)(seed & 0xFFFFFFFFu);
+  key[1] = (uint32_t)(seed >> 32);
+}
+
+/* u_j for request b, position j: 24-bit uniform on [0, 1). */
+double rso_accept_uniform(uint64_t seed, int32_t b, int32_t j) {
+  uint32_t key[2], ctr[4], w[4];
+  seed_key(seed, key);
+  ctr[0] = 0u; ctr[1] = (uint32_t)j; ctr[2] = (uint32_t)b; ctr[3] = 0u;
+  rso_philox4x32_10(ctr, key, w);
+  return (double)(w[0] >> 8) * 0x1p-24;
+}
+
+/* U_x for request b, position j, token x: 23-bit midpoint uniform in (0, 1). */
+double rso_race_uniform(uint64_t seed, int32_t b, int32_t j, int32_t x) {
+  uint32_t key[2], ctr[4], w[4];
+  seed_key(seed, key);
+  ctr[0] = (uint32_t)x >> 2; ctr[1] = (uint32_t)j; ctr[2] = (uint32_t)b; ctr[3] = 1u;
+  rso_philox4x32_10(ctr, key, w);
+  return ((double)(w[x & 3] >> 9) + 0.5) * 0x1p-23;
+}
+
+/* E_x = -ln U_x ~ Exp(1). */
+double rso_race_exponential(uint64_t seed, int32_t b, int32_t j, int32_t x) {
+  return -log(rso_race_uniform(seed, b, j, x));
+}
+
+/* ------------------------------------------------------------------------ */
+static double widen(const void* logits, int dtype, int64_t idx) {
+  if (dtype == RSO_BF16) {
+    uint32_t bits = (uint32_t)((const uint16_t*)logits)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+  }
+  return (double)((const float*)logits)[idx];
+}
+
+/* p = softmax(l / T) of one row, in fp64:
+ *   M = max_y l_y / T,  p_x = exp(l_x / T - M) / sum_y exp(l_y / T - M). */
+void rso_softmax_row(const double* l, int32_t V, double T, double* p) {
+  double M = -INFINITY;
+  for (int32_t x = 0; x < V; ++x) {
+    double s = l[x] / T;
+    if (s > M) M = s;
+  }
+  double Z = 0.0;
+  for (int32_t x = 0; x < V; ++x) {
+    p[x] = exp(l[x] / T - M);
+    Z += p[x];
+  }
+  for (int32_t x = 0; x < V; ++x) p[x] /= Z;
+}
+
+/* Lowest index of the maximum of l. */
+static int32_t argmax_lowest(const double* l, int32_t V) {
+  int32_t best = 0;
+  for (int32_t x = 1; x < V; ++x)
+    if (l[x] > l[best]) best = x;
+  return best;
+}
+
+static void load_row(const void* logits, int dtype, int64_t row, int32_t V, double* l) {
+  for (int32_t x = 0; x < V; ++x) l[x] = widen(logits, dtype, row * (int64_t)V + x);
+}
+
+/* Exponential race over r (r[x] > 0 are the candidates).  Returns the winner
+ * (lowest index among equal keys) or -1 when every r[x] is zero.  *near_tie is
+ * set if the winner's key taken with (rlo, E(1+eps)) does not exceed some
+ * other token's key taken with (rhi, E(1-eps)).  E is scratch of length V. */
+static int32_t race(const double* r, const double* rlo, const double* rhi, int32_t V, uint64_t seed,
+                    int32_t b, int32_t j, double eps, double* E, int* near_tie) {
+  int32_t win = -1;
+  double best = 0.0;
+  for (int32_t x = 0; x < V; ++x) {
+    E[x] = (rhi[x] > 0.0 || r[x] > 0.0) ? rso_race_exponential(seed, b, j, x) : INFINITY;
+    if (!(r[x] > 0.0)) continue;
+    double key = r[x] / E[x];
+    if (win < 0 || key > best) {
+      best = key;
+      win = x;
+    }
+  }
+  *near_tie = 0;
+  if (win < 0) return -1;
+  double lo = rlo[win] / (E[win] * (1.0 + eps));
+  for (int32_t x = 0; x < V; ++x) {
+    if (x == win || !(rhi[x] > 0.0)) continue;
+    double hi = rhi[x] / (E[x] * (1.0 - eps));
+    if (hi >= lo) {
+      *near_tie = 1;
+      break;
+    }
+  }
+  return win;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Verify a batch.
+ *   logits   [R, V] (fp32 or raw bf16 bits), R = D + B; request b owns rows
+ *            cu[b] + b ... cu[b+1] + b (K_b + 1 rows, the last is the bonus row).
+ *   q        [D, V] fp32 draft probabilities, or NULL for one-hot q.
+ *   draft    [D] draft token ids; cu [B+1] prefix sums of draft counts.
+ *   T        [B] temperatures; T <= 0 marks a greedy request.
+ *   greedy_only: treat every request as greedy (T and q ignored).
+ *   out      [B, max_k+1] tokens (-1 padded); num_accepted [B]; flags [B].
+ *   p_draft  [D] or NULL: p(x*) at each evaluated random position, NaN elsewhere.
+ * Returns 0, or -1 on an argument error. */
+int rso_verify(const void* logits, int32_t dtype, const float* q, const int32_t* draft,
+               const int32_t* cu, const float* T, int32_t B, int32_t D, int32_t max_k, int32_t V,
+               uint64_t seed, int32_t greedy_only, double eps, int32_t* out, int32_t* num_accepted,
+               int32_t* flags, double* p_draft, int32_t nthreads) {
+  if (!logits || !draft || !cu || !out || !num_accepted || !flags) return -1;
+  if (!greedy_only && !T) return -1;
+  if (B < 0 || D < 0 || V < 1 || max_k < 0 || (dtype != RSO_F32 && dtype != RSO_BF16)) return -1;
+  if (p_draft)
+    for (int32_t i = 0; i < D; ++i) p_draft[i] = NAN;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* l = (double*)malloc(sizeof(double) * (size_t)V);
+    double* p = (double*)malloc(sizeof(double) * (size_t)V);
+    double* r = (double*)malloc(sizeof(double) * (size_t)V);
+    double* rlo = (double*)malloc(sizeof(double) * (size_t)V);
+    double* rhi = (double*)malloc(sizeof(double) * (size_t)V);
+    double* E = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!l || !p || !r || !rlo || !rhi || !E) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int32_t b = 0; b < B; ++b) {
+      if (failed) continue;
+      int32_t* ob = out + (int64_t)b * (max_k + 1);
+      for (int32_t i = 0; i <= max_k; ++i) ob[i] = -1;
+      num_accepted[b] = -1;
+      flags[b] = 0;
+      int32_t s = cu[b], e = cu[b + 1];
+      int32_t K = e - s;
+      int valid = (s >= 0 && e <= D && K >= 0 && K <= max_k);
+      for (int32_t i = 0; valid && i < K; ++i)
+        if (draft[s + i] < 0 || draft[s + i] >= V) valid = 0;
+      if (!valid) {
+        flags[b] = RSO_FLAG_INVALID;
+        continue;
+      }
+      int64_t row0 = (int64_t)s + b; /* row of position 0 */
+      int greedy = greedy_only || !(T[b] > 0.0f);
+      int32_t n = K, token = -1;
+      if (greedy) {
+        /* accept while draft_j == argmax of row j; emit the argmax at n */
+        for (int32_t j = 0; j < K; ++j) {
+          load_row(logits, dtype, row0 + j, V, l);
+          if (draft[s + j] != argmax_lowest(l, V)) {
+            n = j;
+            break;
+          }
+        }
+        load_row(logits, dtype, row0 + n, V, l);
+        token = argmax_lowest(l, V);
+      } else {
+        double Tb = (double)T[b];
+        for (int32_t j = 0; j < K; ++j) {
+          load_row(logits, dtype, row0 + j, V, l);
+          rso_softmax_row(l, V, Tb, p);
+          int32_t xs = draft[s + j];
+          double qs = q ? (double)q[(int64_t)(s + j) * V + xs] : 1.0;
+          double u = rso_accept_uniform(seed, b, j);
+          double ps = p[xs];
+          if (p_draft) p_draft[s + j] = ps;
+          if (fabs(ps - u * qs) <= eps * ps) flags[b] |= RSO_FLAG_ACCEPT_TIE;
+          if (!(u * qs < ps)) {
+            n = j;
+            break;
+          }
+        }
+        /* p at the sampled position n (bonus row when n == K) */
+        load_row(logits, dtype, row0 + n, V, l);
+        rso_softmax_row(l, V, Tb, p);
+        if (n < K) {
+          int32_t xs = draft[s + n];
+          for (int32_t x = 0; x < V; ++x) {
+            if (q) {
+              double qx = (double)q[(int64_t)(s + n) * V + x];
+              r[x] = fmax(0.0, p[x] - qx);
+              rlo[x] = fmax(0.0, p[x] * (1.0 - eps) - qx);
+              rhi[x] = fmax(0.0, p[x] * (1.0 + eps) - qx);
+            } else {
+              r[x] = (x == xs) ? 0.0 : p[x];
+              rlo[x] = r[x] * (1.0 - eps);
+              rhi[x] = r[x] * (1.0 + eps);
+            }
+          }
+        } else {
+          for (int32_t x = 0; x < V; ++x) {
+            r[x] = p[x];
+            rlo[x] = p[x] * (1.0 - eps);
+            rhi[x] = p[x] * (1.0 + eps);
+          }
+        }
+        int tie = 0;
+        token = race(r, rlo, rhi, V, seed, b, n, eps, E, &tie);
+        if (token < 0) {
+          /* all-zero residual: race over p at the same position */
+          flags[b] |= RSO_FLAG_ZERO_RESIDUAL;
+          for (int32_t x = 0; x < V; ++x) {
+            r[x] = p[x];
+            rlo[x] = p[x] * (1.0 - eps);
+            rhi[x] = p[x] * (1.0 + eps);
+          }
+          token = race(r, rlo, rhi, V, seed, b, n, eps, E, &tie);
+        }
+        if (tie) flags[b] |= RSO_FLAG_RACE_TIE;
+      }
+      for (int32_t i = 0; i < n; ++i) ob[i] = draft[s + i];
+      ob[n] = token;
+      num_accepted[b] = n;
+    }
+    free(l); free(p); free(r); free(rlo); free(rhi); free(E);
+  }
+  return failed ? -1 : 0;
+}
+
+/* Full p = softmax(l / T_b) for every row of every request (rows of greedy
+ * requests, T <= 0, are filled with NaN).  Used to check the library's
+ * optional full-probability output on small shapes. */
+int rso_probs(const void* logits, int32_t dtype, const int32_t* cu, const float* T, int32_t B,
+              int32_t V, double* probs) {
+  if (!logits || !cu || !T || !probs || V < 1) return -1;
+  double* l = (double*)malloc(sizeof(double) * (size_t)V);
+  if (!l) return -1;
+  for (int32_t b = 0; b < B; ++b) {
+    for (int64_t row = (int64_t)cu[b] + b; row <= (int64_t)cu[b + 1] + b; ++row) {
+      double* pr = probs + row * V;
+      if (!(T[b] > 0.0f)) {
+        for (int32_t x = 0; x < V; ++x) pr[x] = NAN;
+        continue;
+      }
+      load_row(logits, dtype, row, V, l);
+      rso_softmax_row(l, V, (double)T[b], pr);
+    }
+  }
+  free(l);
+  return 0;
+}
+
+/* Vector helpers for the statistical pins of the random stream. */
+void rso_accept_uniforms(uint64_t seed, const int32_t* b, const int32_t* j, int64_t n, double* u) {
+  for (int64_t i = 0; i < n; ++i) u[i] = rso_accept_uniform(seed, b[i], j[i]);
+}
+void rso_race_exponentials(uint64_t seed, int32_t b, int32_t j, int32_t x0, int64_t n, double* e) {
+  for (int64_t i = 0; i < n; ++i) e[i] = rso_race_exponential(seed, b, j, (int32_t)(x0 + i));
+}
+
+/* n independent Philox4x32-10 evaluations: ctr [n,4], key [n,2], out [n,4]. */
+void rso_philox_many(int64_t n, const uint32_t* ctr, const uint32_t* key, uint32_t* out) {
+  for (int64_t i = 0; i < n; ++i) rso_philox4x32_10(ctr + 4 * i, key + 2 * i, out + 4 * i);
+}

@@ -1,0 +1,156 @@
+/*
+ * rs_verify.h -- C ABI of the MI355X (gfx950) batched speculative-sampling
+ * verify step.
+ *
+ * The verify step takes the target model's logits for every draft position
+ * plus one bonus position per request, the draft tokens and (optionally) the
+ * draft distributions q, and decides how many drafts each request keeps and
+ * which one extra target token it emits.  Definitions, by page title and
+ * section:
+ *
+ *   - p = softmax(l / T), temperature on the target only
+ *       [第12章 投机解码：以小博大 §12.2.3; §12.9 (compute_probs)]
+ *   - accept draft x* at position j iff u_j * q(x*) < p(x*), u_j ~ U[0,1),
+ *     i.e. with probability min(1, p(x*)/q(x*)); with no q the draft is
+ *     deterministic and q(x*) = 1
+ *       [§12.2.1; 投机解码（Speculative Decoding）端到端深挖 §7.3]
+ *   - drafts after the first rejection are discarded; at the first rejected
+ *     position the extra token is drawn from max(0, p - q) / sum max(0, p - q)
+ *     (no q: p with p(x*) zeroed); if all are accepted it is drawn from p at
+ *     the bonus position
+ *       [§12.2.1 step 3; §12.3.2; §12.9 (recovered tokens)]
+ *   - temperature <= 0 marks a greedy request: accept iff x* == argmax l, the
+ *     extra token is the target argmax
+ *       [§12.2.4; §12.9 (GREEDY_TEMPERATURE sentinel)]
+ *   - ragged batches: flat draft ids with prefix sums cu_num_draft_tokens
+ *       [§12.3.5; vllm v1 源码精读（五） §5.1, §8 (SpecDecodeMetadata)]
+ *   - at most 32 drafts per request per step
+ *       [§12.5.4 (MAX_SPEC_LEN = 32)]
+ *
+ * Random numbers come from counter-based Philox4x32-10 keyed by the 64-bit
+ * seed: accept uniform u_j = (w0 >> 8) 2^-24 with counter (0, j, b, 0); the
+ * sampled token is argmax_x r(x) / E_x with E_x = -ln U_x,
+ * U_x = ((w >> 9) + 1/2) 2^-23, w = word (x & 3) of counter (x >> 2, j, b, 1).
+ * Output is therefore a pure function of (inputs, seed): re-running a call
+ * reproduces it bit for bit.  Vary the seed per decode step.
+ *
+ * Layout (row-major, no padding):
+ *   B = batch, D = total_draft_tokens, R = D + B, V = vocab.
+ *   cu_num_draft_tokens [B+1] int32: cu[0] = 0, cu[b+1] - cu[b] = K_b,
+ *       0 <= K_b <= max_k, cu[B] = D.
+ *   target_logits [R, V] (fp32 or bf16): request b owns rows
+ *       cu[b] + b ... cu[b+1] + b; row cu[b] + b + j scores draft j, the last
+ *       row (j = K_b) is the bonus row.  Uniform K is a plain [B, K+1, V].
+ *   draft_probs [D, V] fp32 (row cu[b] + j = q of draft j of request b), or NULL.
+ *   draft_token_ids [D] int32, temperature [B] fp32.
+ *   output_token_ids [B, max_k+1] int32: the n_b accepted drafts, then the
+ *       extra token, then -1; num_accepted [B] int32 = n_b (n_b + 1 tokens
+ *       are emitted).
+ *
+ * Ownership: every array pointer is a DEVICE pointer owned by the caller; the
+ * library never allocates, frees or keeps a pointer after returning.  Scratch
+ * memory is the caller's workspace (rs_verify_workspace_size bytes, 16-byte
+ * aligned).  All work is enqueued asynchronously on `stream`; the call never
+ * synchronises with the host, so it can be captured in a HIP graph.  Calls
+ * sharing one workspace must not overlap.  The library holds no global state
+ * and is safe to call from several threads on distinct workspaces.
+ *
+ * Errors: every host-side argument check runs before the first HIP call and
+ * returns a status (never aborts, never throws).  Device-resident values are
+ * not read on the host; instead the kernels bound every access by the sizes
+ * given here and treat a request whose metadata is out of range (cu[b] < 0,
+ * cu[b+1] > D, K_b < 0 or > max_k, or a draft id outside [0, V)) as invalid:
+ * its output row is all -1 and num_accepted[b] = -1.  Logits must be finite
+ * or -inf with at least one finite value per row; q must be non-negative;
+ * for T > 0, |l| * log2(e) / T must stay finite in fp32.
+ */
+#ifndef RS_VERIFY_H
+#define RS_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RS_VERIFY_ABI_VERSION 1
+#define RS_MAX_SPEC_LEN 32 /* [第12章 §12.5.4: MAX_SPEC_LEN = 32] */
+
+typedef enum rs_status {
+  RS_OK = 0,
+  RS_ERR_INVALID_ARG = 1, /* NULL pointer, negative size, max_k > 32, D > B*max_k, ... */
+  RS_ERR_UNSUPPORTED = 2, /* unknown dtype, misaligned pointer, size beyond the grid */
+  RS_ERR_WORKSPACE = 3,   /* workspace NULL, misaligned or smaller than required */
+  RS_ERR_HIP = 4          /* a kernel launch or event record failed */
+} rs_status;
+
+typedef enum rs_dtype { RS_F32 = 0, RS_BF16 = 1 } rs_dtype;
+
+/* Optional outputs and knobs for parity checks and profiling.  Pass NULL in
+ * production.  Every pointer may be NULL independently. */
+typedef struct rs_debug {
+  /* [D] device, p(x*) as used by the accept test at every draft position of a
+   * random request (fp64); NaN at greedy requests' positions. */
+  double* draft_target_prob;
+  /* [R, V] device, p at every row of every random request, in the fp32 form
+   * the sampling race uses; rows of greedy requests are left untouched.
+   * Costs an extra pass: small shapes only. */
+  float* probs;
+  /* If non-NULL, events[0..3] are recorded on `stream` before the row pass,
+   * after the row pass, after the scan and after the sampling race. */
+  hipEvent_t* events;
+  /* 0 = automatic.  Otherwise force the row pass to 1, 2, 4, 8 or 16 16-byte
+   * vectors per thread, or the race to 4, 8, 16 or 32 tokens per thread.
+   * Output does not depend on these (the parity tests check that). */
+  int32_t row_vectors_per_thread;
+  int32_t race_tokens_per_thread;
+} rs_debug;
+
+/* Bytes of workspace rs_verify / rs_verify_greedy need for these sizes
+ * (independent of the debug knobs).  Returns 0 for invalid sizes. */
+size_t rs_verify_workspace_size(int32_t batch, int32_t total_draft_tokens, int32_t max_k,
+                                int32_t vocab, rs_dtype logits_dtype);
+
+/* Batched verify (random and greedy requests mixed; T <= 0 is greedy).
+ *   target_logits       [R, V] fp32 or bf16, element-aligned
+ *   draft_probs         [D, V] fp32 or NULL (one-hot q at the draft)
+ *   draft_token_ids     [D] int32
+ *   cu_num_draft_tokens [B+1] int32
+ *   temperature         [B] fp32
+ *   seed                Philox key
+ *   output_token_ids    [B, max_k+1] int32 (written)
+ *   num_accepted        [B] int32 (written)
+ *   workspace           >= rs_verify_workspace_size(...) bytes, 16-byte aligned
+ *   debug               NULL or optional outputs
+ *   stream              HIP stream the kernels are enqueued on
+ * batch = 0 returns RS_OK without touching the GPU. */
+rs_status rs_verify(const void* target_logits, rs_dtype logits_dtype, const float* draft_probs,
+                    const int32_t* draft_token_ids, const int32_t* cu_num_draft_tokens,
+                    const float* temperature, int32_t batch, int32_t total_draft_tokens,
+                    int32_t max_k, int32_t vocab, uint64_t seed, int32_t* output_token_ids,
+                    int32_t* num_accepted, void* workspace, size_t workspace_bytes,
+                    const rs_debug* debug, hipStream_t stream);
+
+/* Greedy argmax-match for every request (no temperature, q or random numbers)
+ * [第12章 §12.2.4; 投机解码（Speculative Decoding）端到端深挖 §7.1 path A].
+ * Same layout, ownership and error rules as rs_verify. */
+rs_status rs_verify_greedy(const void* target_logits, rs_dtype logits_dtype,
+                           const int32_t* draft_token_ids, const int32_t* cu_num_draft_tokens,
+                           int32_t batch, int32_t total_draft_tokens, int32_t max_k, int32_t vocab,
+                           int32_t* output_token_ids, int32_t* num_accepted, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* Static string naming a status. */
+const char* rs_status_string(rs_status status);
+
+/* RS_VERIFY_ABI_VERSION of the built library. */
+int32_t rs_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RS_VERIFY_H */

@@ -1,0 +1,207 @@
+"""MI355X-native batched speculative-sampling verify.
+
+A thin ctypes binding over ``librs_verify.so`` (the C ABI declared in
+``include/rs_verify.h``).  It only marshals arguments: every step of the verify
+path runs in the library's HIP kernels on the caller's current HIP stream.
+PyTorch provides device memory and the stream.
+
+If the library has not been built this module raises on first use; build it
+with ``python -m rejection_sampling_verify_rs_amd.build``.  There is no CPU
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+__all__ = ["verify", "verify_greedy", "workspace_size", "Debug", "RsVerifyError", "load_library",
+           "MAX_SPEC_LEN", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librs_verify.so")
+MAX_SPEC_LEN = 32
+
+RS_OK, RS_ERR_INVALID_ARG, RS_ERR_UNSUPPORTED, RS_ERR_WORKSPACE, RS_ERR_HIP = range(5)
+RS_F32, RS_BF16 = 0, 1
+_DTYPE = {torch.float32: RS_F32, torch.bfloat16: RS_BF16}
+
+_lib = None
+
+
+class RsVerifyError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class _RsDebug(ctypes.Structure):
+    _fields_ = [
+        ("draft_target_prob", ctypes.c_void_p),
+        ("probs", ctypes.c_void_p),
+        ("events", ctypes.c_void_p),
+        ("row_vectors_per_thread", ctypes.c_int32),
+        ("race_tokens_per_thread", ctypes.c_int32),
+    ]
+
+
+def load_library(path: str = LIB_PATH):
+    """Load librs_verify.so once; raise loudly if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m rejection_sampling_verify_rs_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, i32, u64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
+    lib.rs_verify_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.c_int]
+    lib.rs_verify_workspace_size.restype = sz
+    lib.rs_verify.argtypes = [P, ctypes.c_int, P, P, P, P, i32, i32, i32, i32, u64, P, P, P, sz, P, P]
+    lib.rs_verify.restype = ctypes.c_int
+    lib.rs_verify_greedy.argtypes = [P, ctypes.c_int, P, P, i32, i32, i32, i32, P, P, P, sz, P]
+    lib.rs_verify_greedy.restype = ctypes.c_int
+    lib.rs_status_string.argtypes = [ctypes.c_int]
+    lib.rs_status_string.restype = ctypes.c_char_p
+    lib.rs_abi_version.argtypes = []
+    lib.rs_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != RS_OK:
+        msg = load_library().rs_status_string(status).decode()
+        raise RsVerifyError(status, msg)
+
+
+def workspace_size(batch: int, total_draft_tokens: int, max_k: int, vocab: int,
+                   dtype: torch.dtype = torch.bfloat16) -> int:
+    if dtype not in _DTYPE:
+        raise ValueError(f"unsupported logits dtype {dtype}")
+    return int(load_library().rs_verify_workspace_size(batch, total_draft_tokens, max_k, vocab, _DTYPE[dtype]))
+
+
+@dataclass
+class Debug:
+    """Optional parity / profiling outputs (see rs_debug in include/rs_verify.h)."""
+    draft_target_prob: Optional[torch.Tensor] = None  # [D] float64
+    probs: Optional[torch.Tensor] = None              # [R, V] float32
+    events: Optional[Sequence[torch.cuda.Event]] = None  # 4 timing events
+    row_vectors_per_thread: int = 0
+    race_tokens_per_thread: int = 0
+
+    def _struct(self, stream) -> Tuple[_RsDebug, object]:
+        d = _RsDebug()
+        d.draft_target_prob = self.draft_target_prob.data_ptr() if self.draft_target_prob is not None else None
+        d.probs = self.probs.data_ptr() if self.probs is not None else None
+        keep = None
+        if self.events is not None:
+            if len(self.events) != 4:
+                raise ValueError("Debug.events needs 4 events")
+            for e in self.events:  # torch creates the HIP event on first record
+                if e.cuda_event == 0:
+                    e.record(stream)
+            keep = (ctypes.c_void_p * 4)(*[e.cuda_event for e in self.events])
+            d.events = ctypes.cast(keep, ctypes.c_void_p)
+        d.row_vectors_per_thread = int(self.row_vectors_per_thread)
+        d.race_tokens_per_thread = int(self.race_tokens_per_thread)
+        return d, keep
+
+
+def _dev_tensor(t: torch.Tensor, name: str, dtype, device) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _common(target_logits, draft_token_ids, cu_num_draft_tokens, max_k, out, num_accepted, workspace,
+            stream):
+    if not isinstance(target_logits, torch.Tensor) or target_logits.device.type != "cuda":
+        raise ValueError("target_logits must be a CUDA (HIP) tensor")
+    dev = target_logits.device
+    if target_logits.dtype not in _DTYPE:
+        raise TypeError(f"target_logits must be float32 or bfloat16, got {target_logits.dtype}")
+    _dev_tensor(target_logits, "target_logits", None, dev)
+    _dev_tensor(draft_token_ids, "draft_token_ids", torch.int32, dev)
+    _dev_tensor(cu_num_draft_tokens, "cu_num_draft_tokens", torch.int32, dev)
+    if target_logits.dim() < 2:
+        raise ValueError("target_logits must be [R, V] or [B, K+1, V]")
+    V = int(target_logits.shape[-1])
+    B = int(cu_num_draft_tokens.numel()) - 1
+    D = int(draft_token_ids.numel())
+    if B < 0:
+        raise ValueError("cu_num_draft_tokens needs B + 1 entries")
+    if target_logits.numel() != (D + B) * V:
+        raise ValueError(f"target_logits has {target_logits.numel() // max(V, 1)} rows, expected D + B = {D + B}")
+    if max_k is None:
+        raise ValueError("max_k (max drafts per request) is required")
+    if out is None:
+        out = torch.empty((B, max_k + 1), dtype=torch.int32, device=dev)
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    _dev_tensor(out, "out", torch.int32, dev)
+    _dev_tensor(num_accepted, "num_accepted", torch.int32, dev)
+    if out.numel() != B * (max_k + 1) or num_accepted.numel() != B:
+        raise ValueError("out must hold B * (max_k + 1) and num_accepted B int32 values")
+    if workspace is None:
+        n = workspace_size(B, D, max_k, V, target_logits.dtype) if B > 0 else 0
+        workspace = torch.empty((max(n, 1),), dtype=torch.uint8, device=dev)
+    _dev_tensor(workspace, "workspace", torch.uint8, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    return dev, B, D, V, out, num_accepted, workspace, stream
+
+
+def verify(target_logits: torch.Tensor, draft_probs: Optional[torch.Tensor], draft_token_ids: torch.Tensor,
+           cu_num_draft_tokens: torch.Tensor, temperature: torch.Tensor, *, seed: int, max_k: int,
+           out: Optional[torch.Tensor] = None, num_accepted: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None, debug: Optional[Debug] = None,
+           stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Batched verify (rs_verify).  Returns (output_token_ids [B, max_k+1], num_accepted [B])."""
+    lib = load_library()
+    dev, B, D, V, out, num_accepted, workspace, stream = _common(
+        target_logits, draft_token_ids, cu_num_draft_tokens, max_k, out, num_accepted, workspace, stream)
+    _dev_tensor(temperature, "temperature", torch.float32, dev)
+    if temperature.numel() != B:
+        raise ValueError("temperature must have B entries")
+    if draft_probs is not None:
+        _dev_tensor(draft_probs, "draft_probs", torch.float32, dev)
+        if draft_probs.numel() != D * V:
+            raise ValueError("draft_probs must be [D, V]")
+    dbg, keep = (None, None)
+    if debug is not None:
+        dbg, keep = debug._struct(stream)
+    status = lib.rs_verify(
+        target_logits.data_ptr(), _DTYPE[target_logits.dtype],
+        draft_probs.data_ptr() if draft_probs is not None else None,
+        draft_token_ids.data_ptr() if D > 0 else None, cu_num_draft_tokens.data_ptr(), temperature.data_ptr(),
+        B, D, int(max_k), V, int(seed) & ((1 << 64) - 1), out.data_ptr(), num_accepted.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), ctypes.byref(dbg) if dbg is not None else None,
+        ctypes.c_void_p(stream.cuda_stream))
+    del keep
+    _check(status)
+    return out, num_accepted
+
+
+def verify_greedy(target_logits: torch.Tensor, draft_token_ids: torch.Tensor, cu_num_draft_tokens: torch.Tensor,
+                  *, max_k: int, out: Optional[torch.Tensor] = None, num_accepted: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None,
+                  stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Greedy argmax-match verify (rs_verify_greedy)."""
+    lib = load_library()
+    dev, B, D, V, out, num_accepted, workspace, stream = _common(
+        target_logits, draft_token_ids, cu_num_draft_tokens, max_k, out, num_accepted, workspace, stream)
+    status = lib.rs_verify_greedy(
+        target_logits.data_ptr(), _DTYPE[target_logits.dtype], draft_token_ids.data_ptr() if D > 0 else None,
+        cu_num_draft_tokens.data_ptr(), B, D, int(max_k), V, out.data_ptr(), num_accepted.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
+    _check(status)
+    return out, num_accepted

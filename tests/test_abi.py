@@ -1,0 +1,153 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/rs_verify.h declares, and rejects bad arguments on the host before any
+HIP call (NULL pointers, sizes, max_k > 32 [第12章 §12.5.4 MAX_SPEC_LEN],
+dtype, alignment, workspace)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import rejection_sampling_verify_rs_amd as rs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rs_verify.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rs_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return rs.load_library()
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == ["rs_abi_version", "rs_status_string", "rs_verify", "rs_verify_greedy",
+                                     "rs_verify_workspace_size"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    nm = subprocess.run(["nm", "-D", "--defined-only", rs.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (rs_\w+)", nm))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+    assert lib.rs_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.rs_status_string(code).decode().startswith("RS_")
+    assert b"unknown" in lib.rs_status_string(99)
+
+
+def test_workspace_size(lib):
+    n = rs.workspace_size(256, 2048, 8, 151936)
+    assert n > 0 and n % 256 == 0
+    assert rs.workspace_size(256, 2048, 8, 151936, __import__("torch").float32) > 0
+    assert lib.rs_verify_workspace_size(1, 0, 0, 1, 1) > 0
+    assert lib.rs_verify_workspace_size(0, 0, 4, 10, 1) == 0      # empty batch needs nothing
+    assert lib.rs_verify_workspace_size(-1, 0, 4, 10, 1) == 0
+    assert lib.rs_verify_workspace_size(2, 0, 33, 10, 1) == 0     # max_k > 32
+    assert lib.rs_verify_workspace_size(2, 9, 4, 10, 1) == 0      # D > B * max_k
+    assert lib.rs_verify_workspace_size(2, 4, 4, 0, 1) == 0       # V < 1
+    assert lib.rs_verify_workspace_size(2, 4, 4, 10, 5) == 0      # dtype
+    # grows with the batch
+    assert rs.workspace_size(512, 4096, 8, 151936) > n
+
+
+def _gpu_present():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+# The calls below pass non-NULL dummy addresses that are never valid device
+# memory.  Each call must fail validation on the host; they are skipped on a
+# GPU machine so a validation bug can never launch a kernel on them.
+needs_no_gpu = pytest.mark.skipif(_gpu_present(), reason="host-validation tests use dummy pointers")
+
+DUMMY = 0x10000  # 16-byte aligned, never dereferenced
+
+
+def _call(lib, **kw):
+    a = dict(logits=DUMMY, dtype=1, q=None, draft=DUMMY, cu=DUMMY, T=DUMMY, B=2, D=4, max_k=2, V=100, seed=0,
+             out=DUMMY, nacc=DUMMY, ws=DUMMY, ws_bytes=1 << 30, dbg=None, stream=None)
+    a.update(kw)
+    return lib.rs_verify(a["logits"], a["dtype"], a["q"], a["draft"], a["cu"], a["T"], a["B"], a["D"], a["max_k"],
+                         a["V"], a["seed"], a["out"], a["nacc"], a["ws"], a["ws_bytes"], a["dbg"], a["stream"])
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), rs.RS_ERR_INVALID_ARG),
+    (dict(D=-1), rs.RS_ERR_INVALID_ARG),
+    (dict(V=0), rs.RS_ERR_INVALID_ARG),
+    (dict(max_k=-1), rs.RS_ERR_INVALID_ARG),
+    (dict(max_k=33, D=4), rs.RS_ERR_INVALID_ARG),
+    (dict(D=5), rs.RS_ERR_INVALID_ARG),                 # D > B * max_k
+    (dict(dtype=2), rs.RS_ERR_UNSUPPORTED),
+    (dict(logits=None), rs.RS_ERR_INVALID_ARG),
+    (dict(cu=None), rs.RS_ERR_INVALID_ARG),
+    (dict(T=None), rs.RS_ERR_INVALID_ARG),
+    (dict(out=None), rs.RS_ERR_INVALID_ARG),
+    (dict(nacc=None), rs.RS_ERR_INVALID_ARG),
+    (dict(draft=None), rs.RS_ERR_INVALID_ARG),
+    (dict(logits=DUMMY + 1), rs.RS_ERR_UNSUPPORTED),    # bf16 needs 2-byte alignment
+    (dict(logits=DUMMY + 2, dtype=0), rs.RS_ERR_UNSUPPORTED),  # fp32 needs 4-byte alignment
+    (dict(q=DUMMY + 2), rs.RS_ERR_UNSUPPORTED),
+    (dict(cu=DUMMY + 1), rs.RS_ERR_UNSUPPORTED),
+    (dict(ws=None), rs.RS_ERR_WORKSPACE),
+    (dict(ws=DUMMY + 8), rs.RS_ERR_WORKSPACE),
+    (dict(ws_bytes=16), rs.RS_ERR_WORKSPACE),
+])
+def test_host_validation_rejects(lib, kw, status):
+    assert _call(lib, **kw) == status
+
+
+@needs_no_gpu
+def test_empty_batch_is_a_no_op(lib):
+    assert _call(lib, B=0, D=0, logits=None, out=None, nacc=None, ws=None) == rs.RS_OK
+
+
+@needs_no_gpu
+def test_debug_knobs_validated(lib):
+    d = rs._RsDebug()
+    d.row_vectors_per_thread = 3
+    assert _call(lib, dbg=ctypes.byref(d)) == rs.RS_ERR_INVALID_ARG
+    d.row_vectors_per_thread = 0
+    d.race_tokens_per_thread = 12
+    assert _call(lib, dbg=ctypes.byref(d)) == rs.RS_ERR_INVALID_ARG
+
+
+@needs_no_gpu
+def test_greedy_entry_validation(lib):
+    f = lib.rs_verify_greedy
+    ok = dict(logits=DUMMY, dtype=1, draft=DUMMY, cu=DUMMY, B=2, D=4, max_k=2, V=100, out=DUMMY, nacc=DUMMY, ws=DUMMY,
+              ws_bytes=1 << 30)
+
+    def g(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["logits"], a["dtype"], a["draft"], a["cu"], a["B"], a["D"], a["max_k"], a["V"], a["out"],
+                 a["nacc"], a["ws"], a["ws_bytes"], None)
+
+    assert g(max_k=40) == rs.RS_ERR_INVALID_ARG
+    assert g(cu=None) == rs.RS_ERR_INVALID_ARG
+    assert g(ws_bytes=0) == rs.RS_ERR_WORKSPACE
+    assert g(B=0, D=0) == rs.RS_OK
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(3, 10)
+    with pytest.raises(ValueError):
+        rs.verify(x, None, torch.zeros(2, dtype=torch.int32), torch.tensor([0, 2], dtype=torch.int32),
+                  torch.ones(1), seed=0, max_k=2)

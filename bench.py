@@ -34,10 +34,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+
+
 def algorithmic_bytes(w, num_accepted):
-    """Bytes the method must move for one call (see the design notes):
-    every logits row once, the draft ids, q(x*) gathers, the q row at every
-    resampled position, temperatures, cu and the outputs."""
+    """Bytes the method must move for one call, given its outcome.
+
+    every_row: every logits row once (the full-pass definition), plus the
+      q(x*) gathers and draft ids of every position, the q row at every
+      resampled position, temperatures, cu and the outputs.
+    needed: only the rows the verify rule reads -- rows 0 .. n_b of request b
+      (a draft behind the first rejection is discarded unread) -- with the
+      gathers of those positions, plus the same q rows and metadata.
+    logits_every_row / logits_needed: the logits part of each.
+    """
     import numpy as np
     B, D, V = w.B, w.D, w.V
     sl = w.logits.element_size()
@@ -45,10 +54,16 @@ def algorithmic_bytes(w, num_accepted):
     T = w.temperature.cpu().numpy()
     random_req = T > 0
     has_q = w.draft_probs is not None
-    n_res = int(((num_accepted < ks) & random_req).sum()) if has_q else 0
-    logits = (D + B) * V * sl
-    total = logits + D * (4 + (4 if has_q else 0)) + n_res * V * 4 + 4 * B + 4 * (B + 1) + 4 * B * (w.max_k + 2)
-    return total, logits, n_res
+    n = np.asarray(num_accepted)
+    n_res = int(((n < ks) & random_req).sum()) if has_q else 0
+    gather = 4 + (4 if has_q else 0)
+    meta = 4 * B + 4 * (B + 1) + 4 * B * (w.max_k + 2)
+    rows_needed = int((n + 1).sum())
+    evaluated = int(np.minimum(n + 1, ks).sum())
+    every = (D + B) * V * sl + D * gather + n_res * V * 4 + meta
+    needed = rows_needed * V * sl + evaluated * gather + n_res * V * 4 + meta
+    return {"every_row": every, "needed": needed, "logits_every_row": (D + B) * V * sl,
+            "logits_needed": rows_needed * V * sl, "n_res": n_res, "rows_needed": rows_needed}
 
 
 def main():
@@ -59,6 +74,8 @@ def main():
     ap.add_argument("--workload", type=int, default=4, help="1..5 (4 = B=256 K=8 V=151936)")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy (known bytes) to scale HBM byte counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -118,37 +135,85 @@ def main():
     ms_per_step = start.elapsed_time(end) / args.steps
     log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (host wall {wall / args.steps * 1e6:.1f} us/step)")
 
+
     # ---- outcome of each copy (deterministic) -> algorithmic bytes
-    alg, alg_logits, nres, acc = [], [], [], []
+    outcomes, acc = [], []
     for i, w in enumerate(copies):
         call(i)
         torch.cuda.synchronize()
         n = naccs[i].cpu().numpy()
-        a, al, r = algorithmic_bytes(w, n)
-        alg.append(a)
-        alg_logits.append(al)
-        nres.append(r)
+        outcomes.append(algorithmic_bytes(w, n))
         acc.append(float(n.mean()))
-    alg_mean = float(np.mean([alg[k % args.copies] for k in range(args.steps)]))
+    rot = [outcomes[k % args.copies] for k in range(args.steps)]
+    alg_needed = float(np.mean([o["needed"] for o in rot]))
+    alg_every = float(np.mean([o["every_row"] for o in rot]))
     step_s = ms_per_step / 1e3
     positions_per_s = w0.D / step_s
-    eff_gbps = alg_mean / step_s / 1e9
+    per_request = False  # the library's default is the split path
+    alg_path = alg_needed if per_request else alg_every
+    eff_gbps = alg_path / step_s / 1e9
 
     # ---- per-kernel durations with events recorded around each kernel
-    nk = max(10, min(args.steps, 50))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nk)]
-    for k in range(nk):
-        call(k % args.copies, debug=rs.Debug(events=evs[k]))
-    torch.cuda.synchronize()
-    row_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    race_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    row_gbps = alg_logits[0] / (row_ms / 1e3) / 1e9
-    log(f"kernels (event-timed, {nk} calls): row pass {row_ms * 1e3:.1f} us, scan {scan_ms * 1e3:.1f} us, "
-        f"race {race_ms * 1e3:.1f} us")
-    log(f"row pass {row_gbps:.0f} GB/s of logits ({row_gbps / HBM_PEAK_GBPS:.1%} of 8 TB/s); whole call "
-        f"{eff_gbps:.0f} GB/s algorithmic ({eff_gbps / HBM_PEAK_GBPS:.1%}); resampled rows per call {nres}; "
-        f"mean accepted {np.mean(acc):.3f}")
+    def kernel_times(path):
+        nk = max(10, min(args.steps, 50))
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nk)]
+        for k in range(nk):
+            call(k % args.copies, debug=rs.Debug(events=evs[k], sampling_path=path))
+        torch.cuda.synchronize()
+        return [float(np.mean([e[a].elapsed_time(e[a + 1]) for e in evs])) for a in range(3)]
+
+    def timed_steps(path):
+        dbg = rs.Debug(sampling_path=path)
+        for k in range(args.warmup):
+            call(k % args.copies, debug=dbg)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s0.record(stream)
+        for k in range(args.steps):
+            call(k % args.copies, debug=dbg)
+        s1.record(stream)
+        torch.cuda.synchronize()
+        return s0.elapsed_time(s1) / args.steps
+
+    t = kernel_times(0)
+    if per_request:
+        kernels = {"request_kernel": t[0] * 1e3}
+        dom_name, dom_ms, dom_bytes = "request_kernel", t[0], alg_needed
+    else:
+        kernels = {"row_pass": t[0] * 1e3, "scan": t[1] * 1e3, "race_emit": t[2] * 1e3}
+        dom_name, dom_ms = "row_pass_kernel", t[0]
+        dom_bytes = float(np.mean([o["logits_every_row"] for o in rot]))
+    dom_gbps = dom_bytes / (dom_ms / 1e3) / 1e9
+    log(f"kernels (event-timed): " + ", ".join(f"{k} {v:.1f} us" for k, v in kernels.items()))
+    log(f"{dom_name}: {dom_gbps:.0f} GB/s algorithmic ({dom_gbps / HBM_PEAK_GBPS:.1%} of 8 TB/s); "
+        f"whole call {eff_gbps:.0f} GB/s; rows needed per call {[o['rows_needed'] for o in outcomes]} "
+        f"of {w0.D + w0.B}; resampled rows {[o['n_res'] for o in outcomes]}; mean accepted {np.mean(acc):.3f}")
+
+    # the split path (every row's statistics across the GPU, then scan, race, emit) for reference
+    split = None
+    if per_request:
+        ms_split = timed_steps(2)
+        ts = kernel_times(2)
+        lg = float(np.mean([o["logits_every_row"] for o in rot]))
+        split = {"ms_per_step": ms_split, "positions_per_s": w0.D / (ms_split / 1e3),
+                 "achieved_GBps_every_row": alg_every / (ms_split / 1e3) / 1e9,
+                 "kernel_us": {"row_pass": ts[0] * 1e3, "scan": ts[1] * 1e3, "race_emit": ts[2] * 1e3},
+                 "row_pass_GBps": lg / (ts[0] / 1e3) / 1e9}
+        log(f"split path: {ms_split * 1e3:.1f} us/step, {split['positions_per_s']:.3g} positions/s, row pass "
+            f"{split['row_pass_GBps']:.0f} GB/s, kernels {split['kernel_us']}")
+
+    if args.copy_calibration:
+        # a plain elementwise copy kernel of known size (torch.mul by 1 on fp32;
+        # a same-device copy_ would go to the DMA engine, which the counters
+        # do not see): 512 MiB read + 512 MiB written per launch
+        a = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+        c = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.mul(a, 1.0, out=c)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x elementwise copy kernel of 536870912 bytes read + written")
+        del a, c
 
     # ---- CPU oracle on a bounded sample of the same workload
     cpu = None
@@ -192,14 +257,15 @@ def main():
         "config": {"workload": w0.name, "B": w0.B, "K": w0.max_k, "V": w0.V, "total_draft_tokens": w0.D,
                    "logits_dtype": str(w0.logits.dtype).replace("torch.", ""),
                    "draft_probs": w0.draft_probs is not None, "input_copies": args.copies,
-                   "parallelism": "single GPU"},
+                   "path": "per-request" if per_request else "split", "parallelism": "single GPU"},
         "achieved_GBps": eff_gbps,
         "hbm_frac": eff_gbps / HBM_PEAK_GBPS,
-        "algorithmic_bytes_per_step": alg_mean,
-        "kernel_us": {"row_pass": row_ms * 1e3, "scan": scan_ms * 1e3, "race": race_ms * 1e3},
+        "algorithmic_bytes_per_step": {"path": alg_path, "needed": alg_needed, "every_row": alg_every},
+        "kernel_us": kernels,
         "mean_accepted": float(np.mean(acc)),
-        "roofline": {"bound": "hbm", "achieved": row_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": row_gbps / HBM_PEAK_GBPS, "traffic": None, "kernel": "row_pass_kernel"},
+        "roofline": {"bound": "hbm", "achieved": dom_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": dom_gbps / HBM_PEAK_GBPS, "traffic": None, "kernel": dom_name},
+        "split_path": split,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -99,14 +99,22 @@ typedef struct rs_debug {
    * the sampling race uses; rows of greedy requests are left untouched.
    * Costs an extra pass: small shapes only. */
   float* probs;
-  /* If non-NULL, events[0..3] are recorded on `stream` before the row pass,
-   * after the row pass, after the scan and after the sampling race. */
+  /* If non-NULL, events[0..3] are recorded on `stream`: before the first
+   * kernel, after the row pass, after the scan and after sampling on the
+   * split path; before and (three times) after the single kernel on the
+   * per-request path. */
   hipEvent_t* events;
   /* 0 = automatic.  Otherwise force the row pass to 1, 2, 4, 8 or 16 16-byte
-   * vectors per thread, or the race to 4, 8, 16 or 32 tokens per thread.
+   * vectors per thread, or the split race to 4, 8, 16 or 32 tokens per thread.
    * Output does not depend on these (the parity tests check that). */
   int32_t row_vectors_per_thread;
   int32_t race_tokens_per_thread;
+  /* 0 = automatic; 1 = per-request path: one workgroup per request walks its
+   * rows in order, stops at the first rejection, races and writes its row;
+   * 2 = split path: every row's statistics across the whole GPU, then a scan,
+   * a chunked race and an emit kernel.  Requesting `probs` selects the split
+   * path. */
+  int32_t sampling_path;
 } rs_debug;
 
 /* Bytes of workspace rs_verify / rs_verify_greedy need for these sizes

@@ -44,6 +44,7 @@ class _RsDebug(ctypes.Structure):
         ("events", ctypes.c_void_p),
         ("row_vectors_per_thread", ctypes.c_int32),
         ("race_tokens_per_thread", ctypes.c_int32),
+        ("sampling_path", ctypes.c_int32),
     ]
 
 
@@ -91,6 +92,7 @@ class Debug:
     events: Optional[Sequence[torch.cuda.Event]] = None  # 4 timing events
     row_vectors_per_thread: int = 0
     race_tokens_per_thread: int = 0
+    sampling_path: int = 0  # 0 auto, 1 fused, 2 split
 
     def _struct(self, stream) -> Tuple[_RsDebug, object]:
         d = _RsDebug()
@@ -107,6 +109,7 @@ class Debug:
             d.events = ctypes.cast(keep, ctypes.c_void_p)
         d.row_vectors_per_thread = int(self.row_vectors_per_thread)
         d.race_tokens_per_thread = int(self.race_tokens_per_thread)
+        d.sampling_path = int(self.sampling_path)
         return d, keep
 
 

@@ -103,11 +103,22 @@ def test_launch_shapes_give_identical_output():
     w = W.config(4, device="cuda", B=24)
     _say("launch-shape sweep on B=24 K=8 V=151936")
     ref = run_gpu(w)
-    for nv, tpt in [(1, 4), (2, 8), (4, 16), (8, 32), (16, 4)]:
-        g = run_gpu(w, row_nv=nv, race_tpt=tpt)
+    for nv, tpt, path in [(1, 4, 2), (2, 8, 2), (4, 16, 1), (8, 32, 2), (16, 4, 1), (16, 32, 1)]:
+        g = run_gpu(w, row_nv=nv, race_tpt=tpt, path=path)
         np.testing.assert_array_equal(g.tokens, ref.tokens)
         np.testing.assert_array_equal(g.num_accepted, ref.num_accepted)
     compare(ref, run_oracle(w), w)
+
+
+@pytest.mark.parametrize("n", [3, 4])
+def test_fused_and_split_sampling_agree(n):
+    """The fused (one workgroup per request) and split (scan, chunked race, emit)
+    sampling paths give identical output at full size."""
+    w = W.config(n, device="cuda")
+    _say(f"workload {n}: fused vs split sampling")
+    a, b = run_gpu(w, path=1), run_gpu(w, path=2)
+    np.testing.assert_array_equal(a.tokens, b.tokens)
+    np.testing.assert_array_equal(a.num_accepted, b.num_accepted)
 
 
 def test_rerun_is_bit_identical():

@@ -11,9 +11,10 @@ bracketed by a device synchronize.
 
 Prints ONE JSON line on stdout:
   value      verified draft positions per second (D per call / time per call)
-  roofline   the row pass (the dominant kernel): algorithmic bytes (every logits
-             row once) / its average duration, measured with HIP events
-             recorded on the launch stream around that kernel
+  roofline   the longest kernel of the call: the bytes its tasks must move
+             (logits rows it streams, q rows it races) / its average duration,
+             measured with HIP events recorded on the launch stream after
+             every kernel
   cpu_baseline  the CPU oracle timed on this host on a bounded sample
 Diagnostics go to stderr.
 """
@@ -36,34 +37,62 @@ def log(*a):
 
 
 
-def algorithmic_bytes(w, num_accepted):
-    """Bytes the method must move for one call, given its outcome.
+def phase_bounds(max_k, first_phase=0):
+    """Phase boundaries of the library's split path (mirrors its automatic rule:
+    with L = max_k + 1 >= 3 a first phase of positions [0, ceil(L/3)), then the
+    rest; one phase otherwise; first_phase = -1 forces one phase)."""
+    L = max_k + 1
+    if first_phase == -1:
+        return [0, L]
+    p1 = first_phase if first_phase > 0 else ((L + 2) // 3 if L >= 3 else 0)
+    return [0, p1, L] if 0 < p1 < L else [0, L]
 
-    every_row: every logits row once (the full-pass definition), plus the
-      q(x*) gathers and draft ids of every position, the q row at every
-      resampled position, temperatures, cu and the outputs.
-    needed: only the rows the verify rule reads -- rows 0 .. n_b of request b
-      (a draft behind the first rejection is discarded unread) -- with the
-      gathers of those positions, plus the same q rows and metadata.
-    logits_every_row / logits_needed: the logits part of each.
+
+def outcome_bytes(w, num_accepted, bounds):
+    """Bytes each kernel's tasks must move for one call, given the outcome.
+
+    Row statistics of phase i read every logits row of that phase's positions
+    for the requests still active (all requests in phase 1); a race reads the
+    q row of a request resampled with draft probabilities (the logits row it
+    re-reads is not counted: it is an implementation re-read, and usually an
+    Infinity Cache hit).  Also returned: 'needed' = only rows 0 .. n_b of each
+    request (the least any implementation of the rule must read) and
+    'every_row' = every logits row once (what a single phase reads).
     """
     import numpy as np
     B, D, V = w.B, w.D, w.V
     sl = w.logits.element_size()
     ks = np.asarray(w.num_draft)
     T = w.temperature.cpu().numpy()
-    random_req = T > 0
     has_q = w.draft_probs is not None
     n = np.asarray(num_accepted)
-    n_res = int(((n < ks) & random_req).sum()) if has_q else 0
+    rnd = T > 0
+    qrow = np.where(rnd & (n < ks) & has_q, V * 4, 0)  # q row of each resampled request
     gather = 4 + (4 if has_q else 0)
     meta = 4 * B + 4 * (B + 1) + 4 * B * (w.max_k + 2)
+    kernels = []
+    nph = len(bounds) - 1
+    for i in range(nph):
+        jb, je = bounds[i], bounds[i + 1]
+        active = np.ones(B, bool) if i == 0 else (n >= jb)
+        rows = int((active * np.clip(np.minimum(je, ks + 1) - jb, 0, None)).sum())
+        race_q = 0
+        if i >= 1:
+            dec = (n >= bounds[i - 1]) & (n < bounds[i]) & rnd
+            race_q = int(qrow[dec].sum())
+        gathers = int((active * np.clip(np.minimum(je, ks) - jb, 0, None)).sum()) * gather
+        kernels.append(("phase%d" % (i + 1), rows * V * sl + race_q + gathers))
+        kernels.append(("scan%d" % (i + 1), 0))
+    if rnd.any():
+        last = (n >= bounds[nph - 1]) & rnd
+        kernels.append(("race%d" % nph, int(qrow[last].sum())))
+    kernels.append(("emit", meta))
     rows_needed = int((n + 1).sum())
     evaluated = int(np.minimum(n + 1, ks).sum())
-    every = (D + B) * V * sl + D * gather + n_res * V * 4 + meta
-    needed = rows_needed * V * sl + evaluated * gather + n_res * V * 4 + meta
-    return {"every_row": every, "needed": needed, "logits_every_row": (D + B) * V * sl,
-            "logits_needed": rows_needed * V * sl, "n_res": n_res, "rows_needed": rows_needed}
+    needed = rows_needed * V * sl + evaluated * gather + int(qrow.sum()) + meta
+    every = (D + B) * V * sl + D * gather + int(qrow.sum()) + meta
+    return {"kernels": kernels, "total": sum(k[1] for k in kernels), "needed": needed, "every_row": every,
+            "rows_needed": rows_needed, "n_res": int((qrow > 0).sum())}
 
 
 def main():
@@ -136,34 +165,39 @@ def main():
     log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (host wall {wall / args.steps * 1e6:.1f} us/step)")
 
 
-    # ---- outcome of each copy (deterministic) -> algorithmic bytes
+    # ---- outcome of each copy (deterministic) -> bytes each kernel must move
+    bounds = phase_bounds(w0.max_k)
     outcomes, acc = [], []
     for i, w in enumerate(copies):
         call(i)
         torch.cuda.synchronize()
         n = naccs[i].cpu().numpy()
-        outcomes.append(algorithmic_bytes(w, n))
+        outcomes.append(outcome_bytes(w, n, bounds))
         acc.append(float(n.mean()))
     rot = [outcomes[k % args.copies] for k in range(args.steps)]
+    alg_total = float(np.mean([o["total"] for o in rot]))
     alg_needed = float(np.mean([o["needed"] for o in rot]))
     alg_every = float(np.mean([o["every_row"] for o in rot]))
     step_s = ms_per_step / 1e3
     positions_per_s = w0.D / step_s
-    per_request = False  # the library's default is the split path
-    alg_path = alg_needed if per_request else alg_every
-    eff_gbps = alg_path / step_s / 1e9
+    eff_gbps = alg_total / step_s / 1e9
 
-    # ---- per-kernel durations with events recorded around each kernel
-    def kernel_times(path):
-        nk = max(10, min(args.steps, 50))
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nk)]
+    # ---- per-kernel durations: events recorded on the launch stream after every kernel
+    def kernel_times(**knobs):
+        nk = max(10, min(args.steps, 40))
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(16)] for _ in range(nk)]
+        launched = []
         for k in range(nk):
-            call(k % args.copies, debug=rs.Debug(events=evs[k], sampling_path=path))
+            dbg = rs.Debug(events=evs[k], **knobs)
+            call(k % args.copies, debug=dbg)
+            launched.append(dbg.kernels_launched)
         torch.cuda.synchronize()
-        return [float(np.mean([e[a].elapsed_time(e[a + 1]) for e in evs])) for a in range(3)]
+        nl = launched[0]
+        assert all(x == nl for x in launched)
+        return [float(np.mean([e[a].elapsed_time(e[a + 1]) for e in evs])) for a in range(nl)]
 
-    def timed_steps(path):
-        dbg = rs.Debug(sampling_path=path)
+    def timed_steps(**knobs):
+        dbg = rs.Debug(**knobs)
         for k in range(args.warmup):
             call(k % args.copies, debug=dbg)
         s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -175,32 +209,33 @@ def main():
         torch.cuda.synchronize()
         return s0.elapsed_time(s1) / args.steps
 
-    t = kernel_times(0)
-    if per_request:
-        kernels = {"request_kernel": t[0] * 1e3}
-        dom_name, dom_ms, dom_bytes = "request_kernel", t[0], alg_needed
-    else:
-        kernels = {"row_pass": t[0] * 1e3, "scan": t[1] * 1e3, "race_emit": t[2] * 1e3}
-        dom_name, dom_ms = "row_pass_kernel", t[0]
-        dom_bytes = float(np.mean([o["logits_every_row"] for o in rot]))
+    t = kernel_times()
+    names = [k[0] for k in outcomes[0]["kernels"]]
+    if len(t) != len(names):
+        raise RuntimeError(f"library launched {len(t)} kernels, expected {names}")
+    kbytes = [float(np.mean([o["kernels"][i][1] for o in rot])) for i in range(len(names))]
+    kernels = {nm: {"us": ms * 1e3, "task_bytes": by, "GBps": by / (ms / 1e3) / 1e9}
+               for nm, ms, by in zip(names, t, kbytes)}
+    dom = max(range(len(t)), key=lambda i: t[i])
+    dom_name, dom_ms, dom_bytes = names[dom], t[dom], kbytes[dom]
     dom_gbps = dom_bytes / (dom_ms / 1e3) / 1e9
-    log(f"kernels (event-timed): " + ", ".join(f"{k} {v:.1f} us" for k, v in kernels.items()))
-    log(f"{dom_name}: {dom_gbps:.0f} GB/s algorithmic ({dom_gbps / HBM_PEAK_GBPS:.1%} of 8 TB/s); "
-        f"whole call {eff_gbps:.0f} GB/s; rows needed per call {[o['rows_needed'] for o in outcomes]} "
-        f"of {w0.D + w0.B}; resampled rows {[o['n_res'] for o in outcomes]}; mean accepted {np.mean(acc):.3f}")
+    log("kernels (event-timed): " + ", ".join(f"{k} {v['us']:.1f} us ({v['GBps']:.0f} GB/s)"
+                                              for k, v in kernels.items()))
+    log(f"phases {bounds}; whole call {eff_gbps:.0f} GB/s of task bytes; rows needed per call "
+        f"{[o['rows_needed'] for o in outcomes]} of {w0.D + w0.B}; resampled rows {[o['n_res'] for o in outcomes]}; "
+        f"mean accepted {np.mean(acc):.3f}")
 
-    # the split path (every row's statistics across the GPU, then scan, race, emit) for reference
-    split = None
-    if per_request:
-        ms_split = timed_steps(2)
-        ts = kernel_times(2)
-        lg = float(np.mean([o["logits_every_row"] for o in rot]))
-        split = {"ms_per_step": ms_split, "positions_per_s": w0.D / (ms_split / 1e3),
-                 "achieved_GBps_every_row": alg_every / (ms_split / 1e3) / 1e9,
-                 "kernel_us": {"row_pass": ts[0] * 1e3, "scan": ts[1] * 1e3, "race_emit": ts[2] * 1e3},
-                 "row_pass_GBps": lg / (ts[0] / 1e3) / 1e9}
-        log(f"split path: {ms_split * 1e3:.1f} us/step, {split['positions_per_s']:.3g} positions/s, row pass "
-            f"{split['row_pass_GBps']:.0f} GB/s, kernels {split['kernel_us']}")
+    # other configurations of the same call, for reference
+    variants = {}
+    for name, knobs in (("one_phase_every_row", {"first_phase_positions": -1}), ("per_request", {"sampling_path": 1})):
+        ms_v = timed_steps(**knobs)
+        variants[name] = {"ms_per_step": ms_v, "positions_per_s": w0.D / (ms_v / 1e3)}
+        log(f"{name}: {ms_v * 1e3:.1f} us/step, {w0.D / (ms_v / 1e3):.3g} positions/s")
+    tv = kernel_times(first_phase_positions=-1)
+    lg = (w0.D + w0.B) * w0.V * w0.logits.element_size()
+    variants["one_phase_every_row"]["row_pass_us"] = tv[0] * 1e3
+    variants["one_phase_every_row"]["row_pass_GBps"] = lg / (tv[0] / 1e3) / 1e9
+    log(f"one-phase row pass: {tv[0] * 1e3:.1f} us, {lg / (tv[0] / 1e3) / 1e9:.0f} GB/s of logits")
 
     if args.copy_calibration:
         # a plain elementwise copy kernel of known size (torch.mul by 1 on fp32;
@@ -257,15 +292,15 @@ def main():
         "config": {"workload": w0.name, "B": w0.B, "K": w0.max_k, "V": w0.V, "total_draft_tokens": w0.D,
                    "logits_dtype": str(w0.logits.dtype).replace("torch.", ""),
                    "draft_probs": w0.draft_probs is not None, "input_copies": args.copies,
-                   "path": "per-request" if per_request else "split", "parallelism": "single GPU"},
+                   "phases": bounds, "parallelism": "single GPU"},
         "achieved_GBps": eff_gbps,
         "hbm_frac": eff_gbps / HBM_PEAK_GBPS,
-        "algorithmic_bytes_per_step": {"path": alg_path, "needed": alg_needed, "every_row": alg_every},
-        "kernel_us": kernels,
+        "bytes_per_step": {"tasks": alg_total, "needed": alg_needed, "every_row": alg_every},
+        "kernels": kernels,
         "mean_accepted": float(np.mean(acc)),
         "roofline": {"bound": "hbm", "achieved": dom_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": dom_gbps / HBM_PEAK_GBPS, "traffic": None, "kernel": dom_name},
-        "split_path": split,
+        "variants": variants,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

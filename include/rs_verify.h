@@ -92,29 +92,34 @@ typedef enum rs_dtype { RS_F32 = 0, RS_BF16 = 1 } rs_dtype;
 /* Optional outputs and knobs for parity checks and profiling.  Pass NULL in
  * production.  Every pointer may be NULL independently. */
 typedef struct rs_debug {
-  /* [D] device, p(x*) as used by the accept test at every draft position of a
-   * random request (fp64); NaN at greedy requests' positions. */
+  /* [D] device, p(x*) as used by the accept test at every evaluated draft
+   * position of a random request (fp64); NaN at greedy requests' positions;
+   * positions after a request's first rejection may be left unwritten. */
   double* draft_target_prob;
   /* [R, V] device, p at every row of every random request, in the fp32 form
    * the sampling race uses; rows of greedy requests are left untouched.
-   * Costs an extra pass: small shapes only. */
+   * Costs an extra pass over every row (one phase): small shapes only. */
   float* probs;
-  /* If non-NULL, events[0..3] are recorded on `stream`: before the first
-   * kernel, after the row pass, after the scan and after sampling on the
-   * split path; before and (three times) after the single kernel on the
-   * per-request path. */
+  /* num_events caller-created events: events[0] is recorded on `stream`
+   * before the first kernel, events[k] after the k-th kernel launch. */
   hipEvent_t* events;
-  /* 0 = automatic.  Otherwise force the row pass to 1, 2, 4, 8 or 16 16-byte
-   * vectors per thread, or the split race to 4, 8, 16 or 32 tokens per thread.
-   * Output does not depend on these (the parity tests check that). */
+  int32_t num_events;
+  /* HOST pointer or NULL: receives the number of kernels the call launched. */
+  int32_t* kernels_launched;
+  /* 0 = automatic.  Otherwise force the row statistics to 1, 4 or 16 16-byte
+   * vectors per thread, or the race to 8 or 32 tokens per thread.  Output
+   * does not depend on these (the parity tests check that). */
   int32_t row_vectors_per_thread;
   int32_t race_tokens_per_thread;
-  /* 0 = automatic; 1 = per-request path: one workgroup per request walks its
-   * rows in order, stops at the first rejection, races and writes its row;
-   * 2 = split path: every row's statistics across the whole GPU, then a scan,
-   * a chunked race and an emit kernel.  Requesting `probs` selects the split
-   * path. */
+  /* 0 or 2 = phased split path (the default): each phase spreads every
+   * active request's rows across the whole GPU, then scans; 1 = per-request
+   * path: one workgroup per request walks its rows in order and stops at
+   * the first rejection.  Requesting `probs` selects the split path. */
   int32_t sampling_path;
+  /* Split path phases.  0 = automatic (with L = max_k + 1 >= 3, a first phase
+   * of positions [0, ceil(L/3)) and a second of the rest; one phase below);
+   * -1 = one phase (every row is read); k > 0 = first phase [0, k). */
+  int32_t first_phase_positions;
 } rs_debug;
 
 /* Bytes of workspace rs_verify / rs_verify_greedy need for these sizes

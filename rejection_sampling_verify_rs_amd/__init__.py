@@ -42,9 +42,12 @@ class _RsDebug(ctypes.Structure):
         ("draft_target_prob", ctypes.c_void_p),
         ("probs", ctypes.c_void_p),
         ("events", ctypes.c_void_p),
+        ("num_events", ctypes.c_int32),
+        ("kernels_launched", ctypes.c_void_p),
         ("row_vectors_per_thread", ctypes.c_int32),
         ("race_tokens_per_thread", ctypes.c_int32),
         ("sampling_path", ctypes.c_int32),
+        ("first_phase_positions", ctypes.c_int32),
     ]
 
 
@@ -89,27 +92,32 @@ class Debug:
     """Optional parity / profiling outputs (see rs_debug in include/rs_verify.h)."""
     draft_target_prob: Optional[torch.Tensor] = None  # [D] float64
     probs: Optional[torch.Tensor] = None              # [R, V] float32
-    events: Optional[Sequence[torch.cuda.Event]] = None  # 4 timing events
+    events: Optional[Sequence[torch.cuda.Event]] = None  # [0] before the first kernel, [k] after the k-th
     row_vectors_per_thread: int = 0
     race_tokens_per_thread: int = 0
-    sampling_path: int = 0  # 0 auto, 1 fused, 2 split
+    sampling_path: int = 0          # 0 / 2 phased split path, 1 per-request path
+    first_phase_positions: int = 0  # 0 auto, -1 one phase, k > 0 first phase [0, k)
+    kernels_launched: Optional[int] = None  # set after the call
 
     def _struct(self, stream) -> Tuple[_RsDebug, object]:
         d = _RsDebug()
         d.draft_target_prob = self.draft_target_prob.data_ptr() if self.draft_target_prob is not None else None
         d.probs = self.probs.data_ptr() if self.probs is not None else None
-        keep = None
+        count = ctypes.c_int32(0)
+        keep = [count]
         if self.events is not None:
-            if len(self.events) != 4:
-                raise ValueError("Debug.events needs 4 events")
             for e in self.events:  # torch creates the HIP event on first record
                 if e.cuda_event == 0:
                     e.record(stream)
-            keep = (ctypes.c_void_p * 4)(*[e.cuda_event for e in self.events])
-            d.events = ctypes.cast(keep, ctypes.c_void_p)
+            arr = (ctypes.c_void_p * len(self.events))(*[e.cuda_event for e in self.events])
+            keep.append(arr)
+            d.events = ctypes.cast(arr, ctypes.c_void_p)
+            d.num_events = len(self.events)
+        d.kernels_launched = ctypes.cast(ctypes.pointer(count), ctypes.c_void_p)
         d.row_vectors_per_thread = int(self.row_vectors_per_thread)
         d.race_tokens_per_thread = int(self.race_tokens_per_thread)
         d.sampling_path = int(self.sampling_path)
+        d.first_phase_positions = int(self.first_phase_positions)
         return d, keep
 
 
@@ -189,6 +197,8 @@ def verify(target_logits: torch.Tensor, draft_probs: Optional[torch.Tensor], dra
         B, D, int(max_k), V, int(seed) & ((1 << 64) - 1), out.data_ptr(), num_accepted.data_ptr(),
         workspace.data_ptr(), workspace.numel(), ctypes.byref(dbg) if dbg is not None else None,
         ctypes.c_void_p(stream.cuda_stream))
+    if debug is not None:
+        debug.kernels_launched = int(keep[0].value)
     del keep
     _check(status)
     return out, num_accepted

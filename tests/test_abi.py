@@ -125,6 +125,15 @@ def test_debug_knobs_validated(lib):
     d.row_vectors_per_thread = 0
     d.race_tokens_per_thread = 12
     assert _call(lib, dbg=ctypes.byref(d)) == rs.RS_ERR_INVALID_ARG
+    d.race_tokens_per_thread = 0
+    d.sampling_path = 3
+    assert _call(lib, dbg=ctypes.byref(d)) == rs.RS_ERR_INVALID_ARG
+    d.sampling_path = 0
+    d.first_phase_positions = -2
+    assert _call(lib, dbg=ctypes.byref(d)) == rs.RS_ERR_INVALID_ARG
+    d.first_phase_positions = 0
+    d.num_events = 3  # events array missing
+    assert _call(lib, dbg=ctypes.byref(d)) == rs.RS_ERR_INVALID_ARG
 
 
 @needs_no_gpu

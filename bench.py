@@ -37,15 +37,22 @@ def log(*a):
 
 
 
-def phase_bounds(max_k, first_phase=0):
-    """Phase boundaries of the library's split path (mirrors its automatic rule:
-    with L = max_k + 1 >= 3 a first phase of positions [0, ceil(L/3)), then the
-    rest; one phase otherwise; first_phase = -1 forces one phase)."""
+def phase_bounds(max_k, ends=()):
+    """Phase boundaries of the library's split path: its automatic rule (with
+    L = max_k + 1 >= 3, phases [0, ceil(L/3)) and [ceil(L/3), L); one phase
+    otherwise), (-1,) for one phase, or explicit phase ends."""
     L = max_k + 1
-    if first_phase == -1:
+    ends = tuple(ends)
+    if ends and ends[0] < 0:
         return [0, L]
-    p1 = first_phase if first_phase > 0 else ((L + 2) // 3 if L >= 3 else 0)
-    return [0, p1, L] if 0 < p1 < L else [0, L]
+    if not ends or ends[0] == 0:
+        ends = ((L + 2) // 3,) if L >= 3 else ()
+    bounds = [0]
+    for e in ends[:3]:
+        if e <= bounds[-1] or e >= L:
+            break
+        bounds.append(e)
+    return bounds + [L]
 
 
 def outcome_bytes(w, num_accepted, bounds):
@@ -95,6 +102,29 @@ def outcome_bytes(w, num_accepted, bounds):
             "rows_needed": rows_needed, "n_res": int((qrow > 0).sum())}
 
 
+def profiled_traffic(kernel):
+    """HBM bytes per dispatch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE / WRITE_SIZE scaled by a known-size copy kernel), or
+    None if the summary is missing or the kernel sources changed since."""
+    import glob
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "rs_verify_B256_K8_V151936_hbm_bytes.md")
+    if not os.path.exists(path):
+        return None
+    traffic, sha = None, None
+    for line in open(path):
+        if line.startswith("traffic_bytes_per_dispatch:"):
+            traffic = json.loads(line.split(":", 1)[1])
+        elif line.startswith("kernel_source_sha256:"):
+            sha = line.split(":", 1)[1].strip()
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "rejection_sampling_verify_rs_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    if traffic is None or sha != h.hexdigest():
+        return None
+    return traffic.get(kernel)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +133,8 @@ def main():
     ap.add_argument("--workload", type=int, default=4, help="1..5 (4 = B=256 K=8 V=151936)")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget (0 = skip)")
+    ap.add_argument("--phases", default="", help="phase ends, e.g. '3' or '2,5' (default: the library's rule)")
+    ap.add_argument("--sweep", action="store_true", help="also time a set of phase splits (stderr)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (known bytes) to scale HBM byte counters")
     args = ap.parse_args()
@@ -141,8 +173,14 @@ def main():
     naccs = [torch.empty((w.B,), dtype=torch.int32, device=dev) for w in copies]
     stream = torch.cuda.current_stream(dev)
 
+    ends = tuple(int(x) for x in args.phases.split(",") if x.strip())
+
     def call(i, debug=None):
         w = copies[i]
+        if debug is None and ends:
+            debug = rs.Debug(phase_ends=ends)
+        elif debug is not None and ends and not debug.phase_ends:
+            debug.phase_ends = ends
         rs.verify(w.logits, w.draft_probs, w.draft_token_ids, w.cu_num_draft_tokens, w.temperature,
                   seed=w.seed, max_k=w.max_k, out=outs[i], num_accepted=naccs[i], workspace=ws, debug=debug,
                   stream=stream)
@@ -166,7 +204,7 @@ def main():
 
 
     # ---- outcome of each copy (deterministic) -> bytes each kernel must move
-    bounds = phase_bounds(w0.max_k)
+    bounds = phase_bounds(w0.max_k, ends)
     outcomes, acc = [], []
     for i, w in enumerate(copies):
         call(i)
@@ -227,11 +265,15 @@ def main():
 
     # other configurations of the same call, for reference
     variants = {}
-    for name, knobs in (("one_phase_every_row", {"first_phase_positions": -1}), ("per_request", {"sampling_path": 1})):
+    for name, knobs in (("one_phase_every_row", {"phase_ends": (-1,)}), ("per_request", {"sampling_path": 1})):
         ms_v = timed_steps(**knobs)
         variants[name] = {"ms_per_step": ms_v, "positions_per_s": w0.D / (ms_v / 1e3)}
         log(f"{name}: {ms_v * 1e3:.1f} us/step, {w0.D / (ms_v / 1e3):.3g} positions/s")
-    tv = kernel_times(first_phase_positions=-1)
+    if args.sweep:
+        for split in ((1,), (2,), (3,), (4,), (5,), (1, 3), (2, 4), (2, 5), (3, 5), (1, 2, 4), (1, 3, 5), (2, 3, 5)):
+            ms_v = timed_steps(phase_ends=split)
+            log(f"phase ends {split}: {ms_v * 1e3:.1f} us/step, {w0.D / (ms_v / 1e3):.3g} positions/s")
+    tv = kernel_times(phase_ends=(-1,))
     lg = (w0.D + w0.B) * w0.V * w0.logits.element_size()
     variants["one_phase_every_row"]["row_pass_us"] = tv[0] * 1e3
     variants["one_phase_every_row"]["row_pass_GBps"] = lg / (tv[0] / 1e3) / 1e9
@@ -299,7 +341,9 @@ def main():
         "kernels": kernels,
         "mean_accepted": float(np.mean(acc)),
         "roofline": {"bound": "hbm", "achieved": dom_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": dom_gbps / HBM_PEAK_GBPS, "traffic": None, "kernel": dom_name},
+                     "frac": dom_gbps / HBM_PEAK_GBPS,
+                     "traffic": profiled_traffic(dom_name) if w0.name.startswith("B=256 K=8 V=151936") else None,
+                     "kernel": dom_name, "algorithmic_bytes": dom_bytes},
         "variants": variants,
         "cpu_baseline": cpu,
     }

@@ -116,10 +116,12 @@ typedef struct rs_debug {
    * path: one workgroup per request walks its rows in order and stops at
    * the first rejection.  Requesting `probs` selects the split path. */
   int32_t sampling_path;
-  /* Split path phases.  0 = automatic (with L = max_k + 1 >= 3, a first phase
-   * of positions [0, ceil(L/3)) and a second of the rest; one phase below);
-   * -1 = one phase (every row is read); k > 0 = first phase [0, k). */
-  int32_t first_phase_positions;
+  /* Phases of the split path, as the draft positions where phases end.
+   * phase_ends[0] == 0: automatic; phase_ends[0] < 0: one phase (every row
+   * is read); otherwise strictly increasing ends P1 < P2 < ..., stopping at
+   * the first entry that is 0 or >= max_k + 1 (the last phase always ends at
+   * max_k + 1).  At most four phases. */
+  int32_t phase_ends[3];
 } rs_debug;
 
 /* Bytes of workspace rs_verify / rs_verify_greedy need for these sizes

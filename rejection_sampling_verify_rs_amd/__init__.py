@@ -47,7 +47,7 @@ class _RsDebug(ctypes.Structure):
         ("row_vectors_per_thread", ctypes.c_int32),
         ("race_tokens_per_thread", ctypes.c_int32),
         ("sampling_path", ctypes.c_int32),
-        ("first_phase_positions", ctypes.c_int32),
+        ("phase_ends", ctypes.c_int32 * 3),
     ]
 
 
@@ -96,7 +96,7 @@ class Debug:
     row_vectors_per_thread: int = 0
     race_tokens_per_thread: int = 0
     sampling_path: int = 0          # 0 / 2 phased split path, 1 per-request path
-    first_phase_positions: int = 0  # 0 auto, -1 one phase, k > 0 first phase [0, k)
+    phase_ends: Sequence[int] = ()   # () automatic, (-1,) one phase, else positions where phases end
     kernels_launched: Optional[int] = None  # set after the call
 
     def _struct(self, stream) -> Tuple[_RsDebug, object]:
@@ -117,7 +117,9 @@ class Debug:
         d.row_vectors_per_thread = int(self.row_vectors_per_thread)
         d.race_tokens_per_thread = int(self.race_tokens_per_thread)
         d.sampling_path = int(self.sampling_path)
-        d.first_phase_positions = int(self.first_phase_positions)
+        ends = list(self.phase_ends)[:3]
+        for i, v in enumerate(ends):
+            d.phase_ends[i] = int(v)
         return d, keep
 
 

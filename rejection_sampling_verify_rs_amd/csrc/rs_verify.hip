@@ -41,7 +41,7 @@ namespace rsv {
 
 constexpr size_t kRegionAlign = 256;
 constexpr int kTargetBlocks = 2048;  // enough workgroups to fill 256 CUs several times
-constexpr int kMaxPhases = 2;
+constexpr int kMaxPhases = 4;
 
 // ------------------------------------------------------------ phase kernel
 // Grid: n_row row tasks (chunk fastest, then position, then request, so
@@ -186,12 +186,18 @@ static int nsplit_for(int nvec_max, int nv) {
   return n < 1 ? 1 : n;
 }
 
+// End of automatic phase k (1-based) for L = max_k + 1 positions; 0 = none.
+// Two phases: [0, ceil(L/3)) and the rest.
+static int auto_phase_end(int L, int k) {
+  if (L < 3) return 0;
+  return k == 1 ? (L + 2) / 3 : 0;
+}
+
 // Sizes are assumed validated (B >= 1, V >= 1, 0 <= max_k <= 32, 0 <= D <= B * max_k).
 static bool make_plan(int32_t B, int32_t D, int32_t max_k, int32_t V, rs_dtype dt, const rs_debug* dbg, Plan& p) {
   const int force_nv = dbg ? dbg->row_vectors_per_thread : 0;
   const int force_tpt = dbg ? dbg->race_tokens_per_thread : 0;
   const int force_path = dbg ? dbg->sampling_path : 0;
-  const int first_phase = dbg ? dbg->first_phase_positions : 0;
   p.W = dt == RS_BF16 ? 8 : 4;
   p.nvec_max = V / p.W;
   p.nsplit_max = nsplit_for(p.nvec_max, 1);
@@ -218,24 +224,28 @@ static bool make_plan(int32_t B, int32_t D, int32_t max_k, int32_t V, rs_dtype d
   p.race_chunks_max = (int)(((int64_t)V + kRaceThreads * 8 - 1) / (kRaceThreads * 8));
   p.per_request = force_path == 1 && !(dbg && dbg->probs);
   p.request_nt = V >= 65536 ? 1024 : 256;
-  // Phases: positions [0, P1) first, the rest after.  Full probabilities
+  // Phases: position ranges [bounds[i], bounds[i+1]).  A request decided in
+  // one phase never has the rows of later phases read.  Full probabilities
   // need every row, so they force one phase.
   const int L = max_k + 1;
-  int p1 = 0;
-  if (first_phase > 0)
-    p1 = first_phase < L ? first_phase : 0;
-  else if (first_phase == 0 && L >= 3)
-    p1 = (L + 2) / 3;
-  if (dbg && dbg->probs) p1 = 0;
+  p.nphases = 0;
   p.bounds[0] = 0;
-  if (p1 > 0) {
-    p.nphases = 2;
-    p.bounds[1] = p1;
-    p.bounds[2] = L;
+  const int32_t* ends = dbg ? dbg->phase_ends : nullptr;
+  if (dbg && dbg->probs) {
+    // one phase
+  } else if (ends && ends[0] != 0) {
+    for (int k = 0; k < kMaxPhases - 1 && ends[0] > 0; ++k) {
+      if (ends[k] <= p.bounds[p.nphases] || ends[k] >= L) break;
+      p.bounds[++p.nphases] = ends[k];
+    }
   } else {
-    p.nphases = 1;
-    p.bounds[1] = L;
+    for (int k = 1; k < kMaxPhases; ++k) {  // automatic split
+      const int e = auto_phase_end(L, k);
+      if (e <= p.bounds[p.nphases] || e >= L) break;
+      p.bounds[++p.nphases] = e;
+    }
   }
+  p.bounds[++p.nphases] = L;
   p.off_partials = 0;
   p.off_gath = align_up((size_t)R * p.nsplit_max * sizeof(RowPartial));
   p.off_records = p.off_gath + align_up((size_t)(D > 0 ? D : 1) * sizeof(Gathered));
@@ -392,8 +402,7 @@ static rs_status verify_impl(const void* logits, rs_dtype dt, const float* q, co
     if (!(nv == 0 || nv == 1 || nv == 4 || nv == 16)) return RS_ERR_INVALID_ARG;
     if (!(tpt == 0 || tpt == 8 || tpt == 32)) return RS_ERR_INVALID_ARG;
     if (dbg->sampling_path < 0 || dbg->sampling_path > 2) return RS_ERR_INVALID_ARG;
-    if (dbg->first_phase_positions < -1 || dbg->num_events < 0 || (dbg->num_events > 0 && !dbg->events))
-      return RS_ERR_INVALID_ARG;
+    if (dbg->num_events < 0 || (dbg->num_events > 0 && !dbg->events)) return RS_ERR_INVALID_ARG;
     if ((dbg->draft_target_prob && !aligned(dbg->draft_target_prob, 8)) || (dbg->probs && !aligned(dbg->probs, 4)))
       return RS_ERR_UNSUPPORTED;
   }

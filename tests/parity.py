@@ -30,7 +30,7 @@ class GpuResult:
 
 
 def run_gpu(w: W.Workload, *, greedy_entry: bool = False, want_p: bool = False, want_probs: bool = False,
-            row_nv: int = 0, race_tpt: int = 0, path: int = 0, phase: int = 0) -> GpuResult:
+            row_nv: int = 0, race_tpt: int = 0, path: int = 0, phases=()) -> GpuResult:
     dev = torch.device("cuda")
     w = w.to(dev)
     if greedy_entry:
@@ -38,9 +38,9 @@ def run_gpu(w: W.Workload, *, greedy_entry: bool = False, want_p: bool = False, 
         torch.cuda.synchronize()
         return GpuResult(out.cpu().numpy(), n.cpu().numpy())
     dbg = None
-    if want_p or want_probs or row_nv or race_tpt or path or phase:
+    if want_p or want_probs or row_nv or race_tpt or path or phases:
         dbg = rs.Debug(row_vectors_per_thread=row_nv, race_tokens_per_thread=race_tpt, sampling_path=path,
-                       first_phase_positions=phase)
+                       phase_ends=tuple(phases))
         if want_p:
             dbg.draft_target_prob = torch.full((max(w.D, 1),), float("nan"), dtype=torch.float64, device=dev)
         if want_probs:

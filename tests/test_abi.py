@@ -129,9 +129,6 @@ def test_debug_knobs_validated(lib):
     d.sampling_path = 3
     assert _call(lib, dbg=ctypes.byref(d)) == rs.RS_ERR_INVALID_ARG
     d.sampling_path = 0
-    d.first_phase_positions = -2
-    assert _call(lib, dbg=ctypes.byref(d)) == rs.RS_ERR_INVALID_ARG
-    d.first_phase_positions = 0
     d.num_events = 3  # events array missing
     assert _call(lib, dbg=ctypes.byref(d)) == rs.RS_ERR_INVALID_ARG
 

@@ -106,21 +106,22 @@ def test_launch_shapes_give_identical_output():
     o = run_oracle(w)
     compare(ref, o, w)
     ok = ~o.near_tie
-    for nv, tpt, path, phase in [(1, 8, 2, -1), (4, 32, 2, 1), (16, 8, 2, 3), (16, 32, 2, 5), (4, 8, 2, 8),
-                                 (16, 32, 1, 0), (1, 32, 1, 0)]:
-        g = run_gpu(w, row_nv=nv, race_tpt=tpt, path=path, phase=phase)
+    for nv, tpt, path, phases in [(1, 8, 2, (-1,)), (4, 32, 2, (1,)), (16, 8, 2, (3,)), (16, 32, 2, (5,)),
+                                  (4, 8, 2, (8,)), (16, 32, 2, (2, 5)), (4, 32, 2, (1, 3, 6)), (16, 32, 1, ()),
+                                  (1, 32, 1, ())]:
+        g = run_gpu(w, row_nv=nv, race_tpt=tpt, path=path, phases=phases)
         np.testing.assert_array_equal(g.tokens[ok], ref.tokens[ok])
         np.testing.assert_array_equal(g.num_accepted[ok], ref.num_accepted[ok])
 
 
 @pytest.mark.parametrize("n", [3, 4, 5])
-@pytest.mark.parametrize("path,phase", [(1, 0), (2, -1), (2, 2)])
-def test_paths_and_phases_full_size(n, path, phase):
-    """The per-request path, the one-phase split path (every row) and another
-    phase split all match the oracle at full size."""
+@pytest.mark.parametrize("path,phases", [(1, ()), (2, (-1,)), (2, (2,)), (2, (1, 2, 4))])
+def test_paths_and_phases_full_size(n, path, phases):
+    """The per-request path, the one-phase split path (every row) and other
+    phase splits all match the oracle at full size."""
     w = W.config(n, device="cuda")
-    _say(f"workload {n}: path {path}, first phase {phase}")
-    g = run_gpu(w, path=path, phase=phase, want_p=True)
+    _say(f"workload {n}: path {path}, phase ends {phases}")
+    g = run_gpu(w, path=path, phases=phases, want_p=True)
     o = run_oracle(w)
     compare(g, o, w)
     compare_p(g, o)

@@ -4,9 +4,16 @@
 //   resample with q:  r = max(0, p - q)             [§12.2.1 step 3]
 //   resample, no q:   r = p, except r(x*) = 0       [§12.9, last bullet]
 //   bonus:            r = p                         [§12.3.2]
-// with p = exp2(l c - shift) / sum in fp32.  E_x = -ln U_x and the key is
-// r / E'_x with E' = -log2 U = E / ln 2 (a common factor, so the argmax is the
-// same).  Ties go to the lowest token index.
+// with p = exp2(l c - shift) / sum in fp32; without q the factor 1 / sum is
+// common to every token and left out.  E_x = -ln U_x and the key is r / E'_x
+// with E' = -log2 U = E / ln 2 (a common factor, so the argmax is the same).
+// Ties go to the lowest token index.
+//
+// Per token the work is one exp2, one log2 and one reciprocal (each a
+// half-rate transcendental on gfx950) and a handful of full-rate ops; one
+// Philox4x32-10 evaluation (18 v_mad_u64_u32 + XORs) serves four tokens.  The
+// loop body is branch-free: r = 0 gives key 0, which never beats the initial
+// best of 0.
 #pragma once
 
 #include "common.hpp"
@@ -14,35 +21,48 @@
 
 namespace rsv {
 
-// Keys of the four tokens 4G .. 4G+3 of one group from preloaded logits l[]
-// and draft probabilities qv[] (tokens at or beyond V carry l = -inf, so
-// r = 0).  Keeps the thread's best (key, x); tokens are visited in increasing
-// x, so '>' keeps the lowest index among equal keys.
-__device__ __forceinline__ void race_group(const float (&l)[4], const float (&qv)[4], int mode, int32_t exclude,
-                                           float cs, float shift, float inv_sum, uint32_t k0, uint32_t k1,
-                                           uint32_t j, uint32_t b, int32_t G, float& best_key,
-                                           int32_t& best_x) {
+// r(x) for one token, ex = exp2(l c - shift).
+template <int MODE>
+__device__ __forceinline__ float race_weight(float ex, float qv, int32_t x, int32_t exclude, float inv_sum) {
+  if constexpr (MODE == kModeResampleQ) {
+    return fmaxf(fmaf(ex, inv_sum, -qv), 0.f);
+  } else if constexpr (MODE == kModeResampleOneHot) {
+    return x == exclude ? 0.f : ex;
+  } else {
+    return ex;
+  }
+}
+
+// Keys of the four tokens 4G .. 4G+3 from their logits l[] and draft
+// probabilities qv[] (tokens at or beyond V carry l = -inf, so r = 0).  Keeps
+// the thread's best (key, x); tokens arrive in increasing x, so '>' keeps the
+// lowest index among equal keys.
+template <int MODE>
+__device__ __forceinline__ void race_group_m(const float (&l)[4], const float (&qv)[4], int32_t exclude, float cs,
+                                             float shift, float inv_sum, uint32_t k0, uint32_t k1, uint32_t j,
+                                             uint32_t b, int32_t G, float& best_key, int32_t& best_x) {
   const PhiloxOut o = philox4x32_10((uint32_t)G, j, b, 1u, k0, k1);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int32_t x = 4 * G + k;
-    const float ex = exp2_hw(fmaf(l[k], cs, -shift));
-    float r;
-    if (mode == kModeResampleQ)
-      r = fmaxf(ex * inv_sum - qv[k], 0.f);
-    else if (mode == kModeResampleOneHot)
-      r = (x == exclude) ? 0.f : ex;
-    else
-      r = ex;
-    if (r > 0.f) {
-      const float ep = -__builtin_amdgcn_logf(race_uniform_f32(o.w[k]));
-      const float key = r * __builtin_amdgcn_rcpf(ep);
-      if (key > best_key) {
-        best_key = key;
-        best_x = x;
-      }
-    }
+    const float r = race_weight<MODE>(exp2_hw(fmaf(l[k], cs, -shift)), qv[k], x, exclude, inv_sum);
+    const float key = r * __builtin_amdgcn_rcpf(-__builtin_amdgcn_logf(race_uniform_f32(o.w[k])));
+    const bool up = key > best_key;
+    best_key = up ? key : best_key;
+    best_x = up ? x : best_x;
   }
+}
+
+// The same with the mode chosen at run time (per-request path, emit fallback).
+__device__ __forceinline__ void race_group(const float (&l)[4], const float (&qv)[4], int mode, int32_t exclude,
+                                           float cs, float shift, float inv_sum, uint32_t k0, uint32_t k1,
+                                           uint32_t j, uint32_t b, int32_t G, float& best_key, int32_t& best_x) {
+  if (mode == kModeResampleQ)
+    race_group_m<kModeResampleQ>(l, qv, exclude, cs, shift, inv_sum, k0, k1, j, b, G, best_key, best_x);
+  else if (mode == kModeResampleOneHot)
+    race_group_m<kModeResampleOneHot>(l, qv, exclude, cs, shift, inv_sum, k0, k1, j, b, G, best_key, best_x);
+  else
+    race_group_m<kModeBonus>(l, qv, exclude, cs, shift, inv_sum, k0, k1, j, b, G, best_key, best_x);
 }
 
 // Element-wise load of group G (tokens at or beyond V get l = -inf, q = 0).
@@ -57,6 +77,76 @@ __device__ __forceinline__ void load_group_scalar(const Elem* __restrict__ lrow,
   }
 }
 
+// Groups G0 + tid + i * kRaceThreads (i < TPT / 4) of one row.  FULL: every
+// group lies below Gfull (vector-loadable), so loads and arithmetic run
+// unguarded and the loads can be waited on one at a time.
+template <typename Elem, int TPT, int MODE, bool FULL>
+__device__ __forceinline__ void race_span(const Elem* __restrict__ lrow, const float* __restrict__ qrow, int32_t V,
+                                          int32_t G0, int32_t Gfull, int32_t Gend, int32_t exclude, float cs,
+                                          float shift, float inv_sum, uint32_t k0, uint32_t k1, uint32_t j,
+                                          uint32_t b, float& best_key, int32_t& best_x) {
+  constexpr int NG = TPT / 4;
+  constexpr bool kQ = MODE == kModeResampleQ;
+  using R4 = Raw4<Elem>;
+  const int tid = threadIdx.x;
+  typename R4::T lw[NG];
+  float4 qw[NG];
+  // Issue every load of this thread before any arithmetic.
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const int32_t G = G0 + tid + i * kRaceThreads;
+    if (FULL || G < Gfull) {
+      lw[i] = reinterpret_cast<const typename R4::T*>(lrow)[G];
+      if (kQ) qw[i] = reinterpret_cast<const float4*>(qrow)[G];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const int32_t G = G0 + tid + i * kRaceThreads;
+    float l[4], qv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (FULL || G < Gfull) {
+      R4::unpack(lw[i], l);
+      if (kQ) {
+        qv[0] = qw[i].x;
+        qv[1] = qw[i].y;
+        qv[2] = qw[i].z;
+        qv[3] = qw[i].w;
+      }
+    } else if (G < Gend) {
+      load_group_scalar(lrow, kQ ? qrow : nullptr, G, V, l, qv);
+    } else {
+      continue;
+    }
+    race_group_m<MODE>(l, qv, exclude, cs, shift, inv_sum, k0, k1, j, b, G, best_key, best_x);
+  }
+}
+
+template <typename Elem, int TPT, int MODE>
+__device__ __forceinline__ unsigned long long race_chunk_m(const Elem* __restrict__ logits,
+                                                           const float* __restrict__ q, int32_t V, uint64_t seed,
+                                                           const ReqRecord& rec, int32_t b, int32_t c) {
+  constexpr int NG = TPT / 4;  // groups of four tokens per thread
+  using R4 = Raw4<Elem>;
+  __shared__ unsigned long long lds_u[kRaceThreads / 64];
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  const Elem* lrow = logits + (int64_t)rec.row * V;
+  const float* qrow = MODE == kModeResampleQ ? q + ((int64_t)rec.slot0 + rec.n) * V : nullptr;
+  // Vector loads need 8 / 16-byte aligned rows; otherwise every group goes element-wise.
+  const bool fast = ((uintptr_t)lrow % sizeof(typename R4::T)) == 0 && ((uintptr_t)qrow % 16) == 0;
+  const int32_t G0 = c * (kRaceThreads * NG);
+  const int32_t Gend = (V + 3) / 4;
+  const int32_t Gfull = fast ? V / 4 : 0;  // groups loaded as vectors
+  float best_key = 0.f;
+  int32_t best_x = INT_MAX;
+  if (G0 + kRaceThreads * NG <= Gfull)
+    race_span<Elem, TPT, MODE, true>(lrow, qrow, V, G0, Gfull, Gend, rec.exclude, rec.c, rec.shift, rec.inv_sum, k0,
+                                     k1, (uint32_t)rec.n, (uint32_t)b, best_key, best_x);
+  else
+    race_span<Elem, TPT, MODE, false>(lrow, qrow, V, G0, Gfull, Gend, rec.exclude, rec.c, rec.shift, rec.inv_sum,
+                                      k0, k1, (uint32_t)rec.n, (uint32_t)b, best_key, best_x);
+  return block_reduce<kRaceThreads>(pack_key(best_key, best_x), lds_u, MaxOp());
+}
+
 // One workgroup races chunk c (kRaceThreads * TPT tokens) of request b's
 // sampled row described by `rec` and returns the packed best of the chunk
 // (0 = no positive key) in every thread.
@@ -64,52 +154,10 @@ template <typename Elem, int TPT>
 __device__ __forceinline__ unsigned long long race_chunk(const Elem* __restrict__ logits, const float* __restrict__ q,
                                                          int32_t V, uint64_t seed, const ReqRecord& rec, int32_t b,
                                                          int32_t c) {
-  constexpr int NG = TPT / 4;  // groups of four tokens per thread
-  using R4 = Raw4<Elem>;
-  __shared__ unsigned long long lds_u[kRaceThreads / 64];
-  const int tid = threadIdx.x;
-  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-  const Elem* lrow = logits + (int64_t)rec.row * V;
-  const bool has_q = rec.mode == kModeResampleQ;
-  const float* qrow = has_q ? q + ((int64_t)rec.slot0 + rec.n) * V : nullptr;
-  // Vector loads need 8 / 16-byte aligned rows; otherwise every group goes element-wise.
-  const bool fast = ((uintptr_t)lrow % sizeof(typename R4::T)) == 0 && ((uintptr_t)qrow % 16) == 0;
-  const int32_t G0 = c * (kRaceThreads * NG);
-  const int32_t Gend = (V + 3) / 4;
-  const int32_t Gfull = fast ? V / 4 : 0;  // groups loaded as vectors
-
-  // Issue every vector load of this thread before any arithmetic.
-  typename R4::T lw[NG];
-  float4 qw[NG];
-#pragma unroll
-  for (int i = 0; i < NG; ++i) {
-    const int32_t G = G0 + tid + i * kRaceThreads;
-    if (G < Gfull) {
-      lw[i] = reinterpret_cast<const typename R4::T*>(lrow)[G];
-      if (has_q) qw[i] = reinterpret_cast<const float4*>(qrow)[G];
-    }
-  }
-  float best_key = 0.f;
-  int32_t best_x = INT_MAX;
-#pragma unroll
-  for (int i = 0; i < NG; ++i) {
-    const int32_t G = G0 + tid + i * kRaceThreads;
-    if (G < Gend) {
-      float l[4], qv[4];
-      if (G < Gfull) {
-        R4::unpack(lw[i], l);
-        qv[0] = has_q ? qw[i].x : 0.f;
-        qv[1] = has_q ? qw[i].y : 0.f;
-        qv[2] = has_q ? qw[i].z : 0.f;
-        qv[3] = has_q ? qw[i].w : 0.f;
-      } else {
-        load_group_scalar(lrow, qrow, G, V, l, qv);
-      }
-      race_group(l, qv, rec.mode, rec.exclude, rec.c, rec.shift, rec.inv_sum, k0, k1, (uint32_t)rec.n,
-                 (uint32_t)b, G, best_key, best_x);
-    }
-  }
-  return block_reduce<kRaceThreads>(pack_key(best_key, best_x), lds_u, MaxOp());
+  if (rec.mode == kModeResampleQ) return race_chunk_m<Elem, TPT, kModeResampleQ>(logits, q, V, seed, rec, b, c);
+  if (rec.mode == kModeResampleOneHot)
+    return race_chunk_m<Elem, TPT, kModeResampleOneHot>(logits, q, V, seed, rec, b, c);
+  return race_chunk_m<Elem, TPT, kModeBonus>(logits, q, V, seed, rec, b, c);
 }
 
 }  // namespace rsv

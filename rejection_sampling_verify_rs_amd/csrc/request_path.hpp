@@ -19,14 +19,6 @@
 
 namespace rsv {
 
-// One workgroup of NT threads owns one request.  It walks the request's rows
-// in order: a statistics pass over row j (block-wide max and exp-sum, or
-// argmax for greedy requests), then the accept test of draft j; it stops at
-// the first rejection, because rows after it cannot change the output (the
-// drafts behind a rejected one are discarded).  It then races the sampled row
-// (just streamed, so mostly served from the Infinity Cache) and writes the
-// output row.  No state crosses workgroups, so no atomics, fences or extra
-// launches are needed.
 // Block-wide exponential race over one row (see race_group); returns the
 // packed winner (key bits, ~x) or 0 when no residual value is positive.
 template <typename Elem, int NT>

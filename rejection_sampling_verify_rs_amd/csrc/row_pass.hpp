@@ -288,8 +288,31 @@ __device__ __forceinline__ void chunk_task(const Elem* __restrict__ logits, cons
   }
 }
 
+// Partials merged per batch of independent loads (a row has at most this
+// many chunks up to V = 262144 bf16 logits at 16 vectors per thread).
+constexpr int kMergeBatch = 8;
+
 // Merge the nsplit partials of one random row: common shift and fp64 sum.
+// Up to kMergeBatch partials are loaded before any is used, so their
+// latencies overlap.
 __device__ __forceinline__ void merge_random(const RowPartial* P, int nsplit, float& shift, double& S) {
+  if (nsplit <= kMergeBatch) {
+    RowPartial r[kMergeBatch];
+#pragma unroll
+    for (int c = 0; c < kMergeBatch; ++c)
+      if (c < nsplit) r[c] = P[c];
+    float sh = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < kMergeBatch; ++c)
+      if (c < nsplit) sh = fmaxf(sh, r[c].shift);
+    double acc = 0.0;
+#pragma unroll
+    for (int c = 0; c < kMergeBatch; ++c)
+      if (c < nsplit && r[c].sum > 0.0) acc += r[c].sum * exp2((double)r[c].shift - (double)sh);
+    shift = sh;
+    S = acc;
+    return;
+  }
   float sh = -INFINITY;
   for (int c = 0; c < nsplit; ++c) sh = fmaxf(sh, P[c].shift);
   double acc = 0.0;
@@ -303,14 +326,23 @@ __device__ __forceinline__ void merge_random(const RowPartial* P, int nsplit, fl
 __device__ __forceinline__ int32_t merge_greedy(const RowPartial* P, int nsplit) {
   float m = -INFINITY;
   int32_t idx = INT_MAX;
-  for (int c = 0; c < nsplit; ++c) {
-    const float v = P[c].shift;
-    const int32_t a = P[c].argmax;
-    if (a < 0) continue;
-    if (v > m || (v == m && a < idx)) {
-      if (v > m) m = v;
-      idx = a;
+  auto take = [&](const RowPartial& r) {
+    if (r.argmax < 0) return;
+    if (r.shift > m || (r.shift == m && r.argmax < idx)) {
+      m = r.shift;
+      idx = r.argmax;
     }
+  };
+  if (nsplit <= kMergeBatch) {
+    RowPartial r[kMergeBatch];
+#pragma unroll
+    for (int c = 0; c < kMergeBatch; ++c)
+      if (c < nsplit) r[c] = P[c];
+#pragma unroll
+    for (int c = 0; c < kMergeBatch; ++c)
+      if (c < nsplit) take(r[c]);
+  } else {
+    for (int c = 0; c < nsplit; ++c) take(P[c]);
   }
   return idx == INT_MAX ? -1 : idx;
 }

@@ -114,13 +114,14 @@ __global__ __launch_bounds__(64) void emit_kernel(const Elem* __restrict__ logit
                                                   int32_t* __restrict__ out, int32_t* __restrict__ num_accepted) {
   const int32_t b = blockIdx.x;
   const int lane = threadIdx.x;
-  const ReqRecord rec = records[b];
-  if (rec.mode == kModeDone || rec.mode == kModeActive) return;
+  // The chunk winners and the record only depend on b: load them together.
   unsigned long long win = 0ull;
   for (int32_t c = lane; c < nchunks; c += 64) {
     const unsigned long long v = cand[(int64_t)b * nchunks + c];
     win = v > win ? v : win;
   }
+  const ReqRecord rec = records[b];
+  if (rec.mode == kModeDone || rec.mode == kModeActive) return;
   win = wave_max(win);
   if (win == 0ull) {
     const Elem* lrow = logits + (int64_t)rec.row * V;

@@ -29,35 +29,31 @@ __device__ __forceinline__ void scan_phase(
     int32_t j_end, int32_t phase, ReqRecord* __restrict__ records, int32_t* __restrict__ out,
     int32_t* __restrict__ num_accepted, double* __restrict__ dbg_p) {
   const int lane = threadIdx.x & 63;
+  // Loads are grouped by what their addresses depend on (b, then cu[b]) so
+  // each group's latencies overlap.
   const int32_t s = cu[b], e = cu[b + 1];
-  const int32_t K = e - s;
-  int32_t* ob = out + (int64_t)b * (max_k + 1);
-  if (j_begin > 0) {
-    if (records[b].mode != kModeActive) return;  // decided in an earlier phase
-  } else {
-    bool valid = request_valid(s, e, D, max_k);
-    int32_t x = -1;
-    if (valid && lane < K) x = draft[s + lane];
-    valid = valid && (__ballot(valid && lane < K && (x < 0 || x >= V)) == 0ull);
-    if (!valid) {
-      if (lane <= max_k) ob[lane] = -1;
-      if (lane == 0) {
-        num_accepted[b] = -1;
-        records[b].mode = kModeDone;
-      }
-      return;
-    }
-  }
   const float T = greedy_all ? 0.f : temperature[b];
+  if (j_begin > 0 && records[b].mode != kModeActive) return;  // decided in an earlier phase
+  int32_t* ob = out + (int64_t)b * (max_k + 1);
+  if (j_begin == 0 && !request_valid(s, e, D, max_k)) {
+    if (lane <= max_k) ob[lane] = -1;
+    if (lane == 0) {
+      num_accepted[b] = -1;
+      records[b].mode = kModeDone;
+    }
+    return;
+  }
+  const int32_t K = e - s;
   const bool greedy = !(T > 0.f);
   const float cs = greedy ? 0.f : scale_of(T);
-
   const int32_t j = j_begin + lane;
   const bool in_phase = j < j_end && j <= K;
-  const int32_t x = (in_phase && j < K) ? draft[s + j] : -1;
+  // Phase 1 reads every draft id (lane = position) to validate the request.
+  const int32_t x = (j < K && (in_phase || j_begin == 0)) ? draft[s + j] : -1;
   float shift = -INFINITY;
   double S = 0.0;
   int32_t amax = -1;
+  double ps = __builtin_nan("");
   bool accept = false;
   if (in_phase) {
     const int64_t row = (int64_t)s + b + j;
@@ -65,18 +61,25 @@ __device__ __forceinline__ void scan_phase(
     if (greedy) {
       amax = merge_greedy(P, nsplit);
       accept = (j < K) && (x == amax);
-      if (dbg_p && j < K) dbg_p[s + j] = __builtin_nan("");
     } else {
+      const double u = j < K ? accept_uniform(seed, b, j) : 0.0;
+      const Gathered g = j < K ? gath[s + j] : Gathered{0.f, 0.f};
       merge_random(P, nsplit, shift, S);
       if (j < K) {
-        const Gathered g = gath[s + j];
-        const double ps = exp2((double)g.lstar * (double)cs - (double)shift) / S;
-        const double u = accept_uniform(seed, b, j);
+        ps = exp2((double)g.lstar * (double)cs - (double)shift) / S;
         accept = u * (double)g.qstar < ps;
-        if (dbg_p) dbg_p[s + j] = ps;
       }
     }
   }
+  if (j_begin == 0 && __ballot(j < K && (x < 0 || x >= V))) {  // a draft id out of range
+    if (lane <= max_k) ob[lane] = -1;
+    if (lane == 0) {
+      num_accepted[b] = -1;
+      records[b].mode = kModeDone;
+    }
+    return;
+  }
+  if (dbg_p && in_phase && j < K) dbg_p[s + j] = ps;
   const unsigned long long rej = __ballot(in_phase && j < K && !accept);
   int32_t n;
   if (rej) {

@@ -1,24 +1,31 @@
 #!/usr/bin/env python3
 """Benchmark of the batched speculative-sampling verify step on one MI355X.
 
-One step = one rs_verify call over a whole batch (row pass, scan, sampling
-race).  The default workload is B=256 requests, K=8 drafts each, V=151936,
-bf16 target logits, fp32 draft probabilities, per-request temperature
-~U[0.3, 1.2], mean acceptance ~0.75.  Inputs are built on the GPU before the
-timed region (three independent copies, rotated so consecutive calls do not
-hit the 256 MB Infinity Cache); the timed region holds exactly --steps calls
-bracketed by a device synchronize.
+One step = one rs_verify call over a whole batch (row statistics, accept
+tests, first rejection, sampling race, output rows).  The default workload is
+B=256 requests, K=8 drafts each, V=151936, bf16 target logits, fp32 draft
+probabilities, per-request temperature ~U[0.3, 1.2], mean acceptance ~0.75.
+Inputs are built on the GPU before the timed region (three independent
+copies, rotated so consecutive calls do not hit the 256 MB Infinity Cache);
+the timed region holds exactly --steps calls bracketed by a device
+synchronize.
 
 Prints ONE JSON line on stdout:
-  value      verified draft positions per second (D per call / time per call)
-  roofline   the longest kernel of the call: the bytes its tasks must move
-             (logits rows it streams, q rows it races) / its average duration,
-             measured with HIP events recorded on the launch stream after
-             every kernel
-  cpu_baseline  the CPU oracle timed on this host on a bounded sample
+  value           verified draft positions per second (D per call / time)
+  effective_GBps  every logits row once + gathers + resampled q rows +
+                  metadata, over the call time (rows skipped behind a first
+                  rejection still count)
+  achieved_GBps   the bytes the call's kernels must move (rows 0 .. n_b of
+                  each request on the stream path) over the call time
+  roofline        the longest kernel of the call: the bytes it must move /
+                  its average duration, measured with HIP events recorded on
+                  the launch stream after every kernel; `traffic` is the HBM
+                  bytes rocprofv3 counted for it (profiles/)
+  cpu_baseline    the CPU oracle timed on this host on a bounded sample
 Diagnostics go to stderr.
 """
 import argparse
+import gc
 import json
 import os
 import sys
@@ -55,16 +62,25 @@ def phase_bounds(max_k, ends=()):
     return bounds + [L]
 
 
-def outcome_bytes(w, num_accepted, bounds):
+def outcome_bytes(w, num_accepted, bounds, path=2):
     """Bytes each kernel's tasks must move for one call, given the outcome.
 
-    Row statistics of phase i read every logits row of that phase's positions
+    Phased split path (2): per phase i a row kernel (phase1: rows; phase2..:
+    rows + the race of the previous phase's decisions) and its scan (accept
+    tests), then race<last> (the race of the last phase's decisions) and emit
+    (output rows of random requests).  Row
+    statistics of phase i read every logits row of that phase's positions
     for the requests still active (all requests in phase 1); a race reads the
     q row of a request resampled with draft probabilities (the logits row it
     re-reads is not counted: it is an implementation re-read, and usually an
-    Infinity Cache hit).  Also returned: 'needed' = only rows 0 .. n_b of each
-    request (the least any implementation of the rule must read) and
-    'every_row' = every logits row once (what a single phase reads).
+    Infinity Cache hit).
+    Per-request path (1): one kernel, charged with the 'needed' bytes.
+    Stream path (3): init (per-request set-up), stream (charged with all the
+    'needed' bytes; rows it reads speculatively are not counted) and
+    race_tail (race chunks left to after the stream kernel, charged nothing).
+    Also returned: 'needed' = only rows 0 .. n_b of each request (the least
+    any implementation of the rule must read) and 'every_row' = every logits
+    row once (what a single phase reads).
     """
     import numpy as np
     B, D, V = w.B, w.D, w.V
@@ -77,27 +93,31 @@ def outcome_bytes(w, num_accepted, bounds):
     qrow = np.where(rnd & (n < ks) & has_q, V * 4, 0)  # q row of each resampled request
     gather = 4 + (4 if has_q else 0)
     meta = 4 * B + 4 * (B + 1) + 4 * B * (w.max_k + 2)
-    kernels = []
-    nph = len(bounds) - 1
-    for i in range(nph):
-        jb, je = bounds[i], bounds[i + 1]
-        active = np.ones(B, bool) if i == 0 else (n >= jb)
-        rows = int((active * np.clip(np.minimum(je, ks + 1) - jb, 0, None)).sum())
-        race_q = 0
-        if i >= 1:
-            dec = (n >= bounds[i - 1]) & (n < bounds[i]) & rnd
-            race_q = int(qrow[dec].sum())
-        gathers = int((active * np.clip(np.minimum(je, ks) - jb, 0, None)).sum()) * gather
-        kernels.append(("phase%d" % (i + 1), rows * V * sl + race_q + gathers))
-        kernels.append(("scan%d" % (i + 1), 0))
-    if rnd.any():
-        last = (n >= bounds[nph - 1]) & rnd
-        kernels.append(("race%d" % nph, int(qrow[last].sum())))
-    kernels.append(("emit", meta))
     rows_needed = int((n + 1).sum())
     evaluated = int(np.minimum(n + 1, ks).sum())
     needed = rows_needed * V * sl + evaluated * gather + int(qrow.sum()) + meta
     every = (D + B) * V * sl + D * gather + int(qrow.sum()) + meta
+    kernels = []
+    if path == 1:
+        kernels = [("request", needed)]
+    elif path == 3:
+        kernels = [("init", 0), ("stream", needed), ("race_tail", 0)]
+    else:
+        nph = len(bounds) - 1
+        for i in range(nph):
+            jb, je = bounds[i], bounds[i + 1]
+            active = np.ones(B, bool) if i == 0 else (n >= jb)
+            rows = int((active * np.clip(np.minimum(je, ks + 1) - jb, 0, None)).sum())
+            race_q = 0
+            if i >= 1:
+                dec = (n >= bounds[i - 1]) & (n < bounds[i]) & rnd
+                race_q = int(qrow[dec].sum())
+            gathers = int((active * np.clip(np.minimum(je, ks) - jb, 0, None)).sum()) * gather
+            kernels.append(("phase%d" % (i + 1), rows * V * sl + race_q + gathers))
+            kernels.append(("scan%d" % (i + 1), 0))
+        last = (n >= bounds[nph - 1]) & rnd
+        kernels.append(("race%d" % nph, int(qrow[last].sum())))
+        kernels.append(("emit", meta))
     return {"kernels": kernels, "total": sum(k[1] for k in kernels), "needed": needed, "every_row": every,
             "rows_needed": rows_needed, "n_res": int((qrow > 0).sum())}
 
@@ -128,8 +148,8 @@ def profiled_traffic(kernel):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", type=int, default=4, help="1..5 (4 = B=256 K=8 V=151936)")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget (0 = skip)")
@@ -168,7 +188,8 @@ def main():
         f"{'' if w0.draft_probs is None else f', {w0.draft_probs.numel() * 4 / 1e6:.1f} MB q'}) "
         f"built in {time.time() - t0:.1f}s")
 
-    ws = torch.empty(rs.workspace_size(w0.B, w0.D, w0.max_k, w0.V, w0.logits.dtype), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(rs.workspace_size(w.B, w.D, w.max_k, w.V, w.logits.dtype) for w in copies),
+                     dtype=torch.uint8, device=dev)
     outs = [torch.empty((w.B, w.max_k + 1), dtype=torch.int32, device=dev) for w in copies]
     naccs = [torch.empty((w.B,), dtype=torch.int32, device=dev) for w in copies]
     stream = torch.cuda.current_stream(dev)
@@ -185,12 +206,16 @@ def main():
                   seed=w.seed, max_k=w.max_k, out=outs[i], num_accepted=naccs[i], workspace=ws, debug=debug,
                   stream=stream)
 
+    # Warm-up runs straight into the timed region (the GPU's clocks drop after
+    # even a few milliseconds idle), with no garbage-collection pauses on the
+    # launching thread meanwhile.
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gc.collect()
+    gc.disable()
     for k in range(args.warmup):
         call(k % args.copies)
-    torch.cuda.synchronize()
 
     # ---- timed region: exactly --steps calls
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
@@ -199,18 +224,23 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    gc.enable()
     ms_per_step = start.elapsed_time(end) / args.steps
     log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (host wall {wall / args.steps * 1e6:.1f} us/step)")
 
 
     # ---- outcome of each copy (deterministic) -> bytes each kernel must move
     bounds = phase_bounds(w0.max_k, ends)
+    probe = rs.Debug()
+    call(0, debug=probe)
+    path = probe.path_taken
+    path_name = {1: "per-request", 2: "phased split", 3: "stream"}[path]
     outcomes, acc = [], []
     for i, w in enumerate(copies):
         call(i)
         torch.cuda.synchronize()
         n = naccs[i].cpu().numpy()
-        outcomes.append(outcome_bytes(w, n, bounds))
+        outcomes.append(outcome_bytes(w, n, bounds, path))
         acc.append(float(n.mean()))
     rot = [outcomes[k % args.copies] for k in range(args.steps)]
     alg_total = float(np.mean([o["total"] for o in rot]))
@@ -219,12 +249,19 @@ def main():
     step_s = ms_per_step / 1e3
     positions_per_s = w0.D / step_s
     eff_gbps = alg_total / step_s / 1e9
+    # The method's algorithmic bytes (every logits row once, gathers, the q row
+    # of every resampled request, metadata) over the call time: rows skipped
+    # behind a first rejection still count, so this "effective" rate can
+    # exceed what the call physically moves.
+    every_gbps = alg_every / step_s / 1e9
 
     # ---- per-kernel durations: events recorded on the launch stream after every kernel
     def kernel_times(**knobs):
         nk = max(10, min(args.steps, 40))
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(16)] for _ in range(nk)]
         launched = []
+        for k in range(args.warmup):
+            call(k % args.copies, debug=rs.Debug(**knobs))
         for k in range(nk):
             dbg = rs.Debug(events=evs[k], **knobs)
             call(k % args.copies, debug=dbg)
@@ -236,15 +273,17 @@ def main():
 
     def timed_steps(**knobs):
         dbg = rs.Debug(**knobs)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gc.disable()
         for k in range(args.warmup):
             call(k % args.copies, debug=dbg)
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         s0.record(stream)
         for k in range(args.steps):
             call(k % args.copies, debug=dbg)
         s1.record(stream)
         torch.cuda.synchronize()
+        gc.enable()
         return s0.elapsed_time(s1) / args.steps
 
     t = kernel_times()
@@ -259,13 +298,17 @@ def main():
     dom_gbps = dom_bytes / (dom_ms / 1e3) / 1e9
     log("kernels (event-timed): " + ", ".join(f"{k} {v['us']:.1f} us ({v['GBps']:.0f} GB/s)"
                                               for k, v in kernels.items()))
-    log(f"phases {bounds}; whole call {eff_gbps:.0f} GB/s of task bytes; rows needed per call "
+    log(f"path: {path_name}; effective {every_gbps:.0f} GB/s (every row once, {every_gbps / HBM_PEAK_GBPS:.1%} of "
+        f"peak); {eff_gbps:.0f} GB/s of needed / task bytes; rows needed per call "
         f"{[o['rows_needed'] for o in outcomes]} of {w0.D + w0.B}; resampled rows {[o['n_res'] for o in outcomes]}; "
         f"mean accepted {np.mean(acc):.3f}")
 
     # other configurations of the same call, for reference
     variants = {}
-    for name, knobs in (("one_phase_every_row", {"phase_ends": (-1,)}), ("per_request", {"sampling_path": 1})):
+    for name, knobs in (("phased_split", {"sampling_path": 2}),
+                        ("stream", {"sampling_path": 3}),
+                        ("one_phase_every_row", {"sampling_path": 2, "phase_ends": (-1,)}),
+                        ("per_request", {"sampling_path": 1})):
         ms_v = timed_steps(**knobs)
         variants[name] = {"ms_per_step": ms_v, "positions_per_s": w0.D / (ms_v / 1e3)}
         log(f"{name}: {ms_v * 1e3:.1f} us/step, {w0.D / (ms_v / 1e3):.3g} positions/s")
@@ -273,7 +316,7 @@ def main():
         for split in ((1,), (2,), (3,), (4,), (5,), (1, 3), (2, 4), (2, 5), (3, 5), (1, 2, 4), (1, 3, 5), (2, 3, 5)):
             ms_v = timed_steps(phase_ends=split)
             log(f"phase ends {split}: {ms_v * 1e3:.1f} us/step, {w0.D / (ms_v / 1e3):.3g} positions/s")
-    tv = kernel_times(phase_ends=(-1,))
+    tv = kernel_times(sampling_path=2, phase_ends=(-1,))
     lg = (w0.D + w0.B) * w0.V * w0.logits.element_size()
     variants["one_phase_every_row"]["row_pass_us"] = tv[0] * 1e3
     variants["one_phase_every_row"]["row_pass_GBps"] = lg / (tv[0] / 1e3) / 1e9
@@ -334,7 +377,9 @@ def main():
         "config": {"workload": w0.name, "B": w0.B, "K": w0.max_k, "V": w0.V, "total_draft_tokens": w0.D,
                    "logits_dtype": str(w0.logits.dtype).replace("torch.", ""),
                    "draft_probs": w0.draft_probs is not None, "input_copies": args.copies,
-                   "phases": bounds, "parallelism": "single GPU"},
+                   "path": path_name, "phases": bounds if path == 2 else None, "parallelism": "single GPU"},
+        "effective_GBps": every_gbps,
+        "effective_frac": every_gbps / HBM_PEAK_GBPS,
         "achieved_GBps": eff_gbps,
         "hbm_frac": eff_gbps / HBM_PEAK_GBPS,
         "bytes_per_step": {"tasks": alg_total, "needed": alg_needed, "every_row": alg_every},

@@ -94,7 +94,7 @@ typedef enum rs_dtype { RS_F32 = 0, RS_BF16 = 1 } rs_dtype;
 typedef struct rs_debug {
   /* [D] device, p(x*) as used by the accept test at every evaluated draft
    * position of a random request (fp64); NaN at greedy requests' positions;
-   * positions after a request's first rejection may be left unwritten. */
+   * positions after a request's first rejection may or may not be written. */
   double* draft_target_prob;
   /* [R, V] device, p at every row of every random request, in the fp32 form
    * the sampling race uses; rows of greedy requests are left untouched.
@@ -111,17 +111,26 @@ typedef struct rs_debug {
    * does not depend on these (the parity tests check that). */
   int32_t row_vectors_per_thread;
   int32_t race_tokens_per_thread;
-  /* 0 or 2 = phased split path (the default): each phase spreads every
-   * active request's rows across the whole GPU, then scans; 1 = per-request
-   * path: one workgroup per request walks its rows in order and stops at
-   * the first rejection.  Requesting `probs` selects the split path. */
+  /* 0 = automatic: the stream path when B times the V-chunks per row is at
+   * least 1024, else the phased split path.  1 = per-request path: one
+   * workgroup per request walks its rows in order and stops at the first
+   * rejection.  2 = phased split path: each phase spreads every active
+   * request's rows across the whole GPU, then scans.  3 = stream path: one
+   * kernel streams rows position by position, decides requests as their
+   * rows complete (skipping the rows behind a decided request's first
+   * rejection) and races them as they are decided.  Requesting `probs`
+   * selects the split path. */
   int32_t sampling_path;
   /* Phases of the split path, as the draft positions where phases end.
    * phase_ends[0] == 0: automatic; phase_ends[0] < 0: one phase (every row
    * is read); otherwise strictly increasing ends P1 < P2 < ..., stopping at
    * the first entry that is 0 or >= max_k + 1 (the last phase always ends at
-   * max_k + 1).  At most four phases. */
+   * max_k + 1).  At most four phases.  On the stream path phase_ends[0] > 0
+   * is the number of positions streamed before race tasks start to
+   * interleave with rows (default max_k). */
   int32_t phase_ends[3];
+  /* HOST pointer or NULL: receives the path the call took (1, 2 or 3). */
+  int32_t* path_taken;
 } rs_debug;
 
 /* Bytes of workspace rs_verify / rs_verify_greedy need for these sizes

@@ -48,6 +48,7 @@ class _RsDebug(ctypes.Structure):
         ("race_tokens_per_thread", ctypes.c_int32),
         ("sampling_path", ctypes.c_int32),
         ("phase_ends", ctypes.c_int32 * 3),
+        ("path_taken", ctypes.c_void_p),
     ]
 
 
@@ -95,16 +96,18 @@ class Debug:
     events: Optional[Sequence[torch.cuda.Event]] = None  # [0] before the first kernel, [k] after the k-th
     row_vectors_per_thread: int = 0
     race_tokens_per_thread: int = 0
-    sampling_path: int = 0          # 0 / 2 phased split path, 1 per-request path
+    sampling_path: int = 0          # 0 automatic, 1 per-request, 2 phased split, 3 stream
     phase_ends: Sequence[int] = ()   # () automatic, (-1,) one phase, else positions where phases end
     kernels_launched: Optional[int] = None  # set after the call
+    path_taken: Optional[int] = None        # set after the call: 1, 2 or 3
 
     def _struct(self, stream) -> Tuple[_RsDebug, object]:
         d = _RsDebug()
         d.draft_target_prob = self.draft_target_prob.data_ptr() if self.draft_target_prob is not None else None
         d.probs = self.probs.data_ptr() if self.probs is not None else None
         count = ctypes.c_int32(0)
-        keep = [count]
+        path = ctypes.c_int32(0)
+        keep = [count, path]
         if self.events is not None:
             for e in self.events:  # torch creates the HIP event on first record
                 if e.cuda_event == 0:
@@ -114,6 +117,7 @@ class Debug:
             d.events = ctypes.cast(arr, ctypes.c_void_p)
             d.num_events = len(self.events)
         d.kernels_launched = ctypes.cast(ctypes.pointer(count), ctypes.c_void_p)
+        d.path_taken = ctypes.cast(ctypes.pointer(path), ctypes.c_void_p)
         d.row_vectors_per_thread = int(self.row_vectors_per_thread)
         d.race_tokens_per_thread = int(self.race_tokens_per_thread)
         d.sampling_path = int(self.sampling_path)
@@ -201,6 +205,7 @@ def verify(target_logits: torch.Tensor, draft_probs: Optional[torch.Tensor], dra
         ctypes.c_void_p(stream.cuda_stream))
     if debug is not None:
         debug.kernels_launched = int(keep[0].value)
+        debug.path_taken = int(keep[1].value)
     del keep
     _check(status)
     return out, num_accepted

@@ -174,6 +174,45 @@ __device__ __forceinline__ bool request_valid(int32_t s, int32_t e, int32_t D, i
   return s >= 0 && s <= e && e <= D && e - s <= max_k;
 }
 
+// Hand-off between workgroups of one kernel (the stream path).  Data is
+// written with agent-scope atomic stores, which write through the XCD's L2 to
+// the device-coherent level, and read back with agent-scope atomic loads,
+// which do not hit a stale L2 line.  A producer waits until its stores have
+// been acknowledged (s_waitcnt) before it bumps an arrival counter, and a
+// consumer reads only after observing the counter or flag.  No L2 writeback
+// or invalidate (a device fence) is needed, because nothing handed over this
+// way sits in an L2 as a dirty or stale line.
+__device__ __forceinline__ void store_coherent(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long load_coherent(const unsigned long long* p) {
+  return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent32(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_coherent32(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long atomic_or64(unsigned long long* p, unsigned long long v) {
+  return __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Compare-and-swap; true if *p held `expected` and now holds `desired`.
+__device__ __forceinline__ bool atomic_cas32(int32_t* p, int32_t expected, int32_t desired) {
+  return __hip_atomic_compare_exchange_strong(p, &expected, desired, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait for every memory access this wavefront has issued (stores included).
+__device__ __forceinline__ void wait_memory() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Arrival counter: true in exactly one caller, the last of `total`.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t total) {
+  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == total - 1u;
+}
+
 // Race keys order as unsigned integers: (fp32 bits of the positive key) << 32
 // | ~x, so the maximum is the largest key and, among equal keys, the lowest x.
 // 0 means "no positive key".

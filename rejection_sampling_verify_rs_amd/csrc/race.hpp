@@ -53,7 +53,7 @@ __device__ __forceinline__ void race_group_m(const float (&l)[4], const float (&
   }
 }
 
-// The same with the mode chosen at run time (per-request path, emit fallback).
+// The same with the mode chosen at run time (per-request path, output fallback).
 __device__ __forceinline__ void race_group(const float (&l)[4], const float (&qv)[4], int mode, int32_t exclude,
                                            float cs, float shift, float inv_sum, uint32_t k0, uint32_t k1,
                                            uint32_t j, uint32_t b, int32_t G, float& best_key, int32_t& best_x) {
@@ -159,5 +159,41 @@ __device__ __forceinline__ unsigned long long race_chunk(const Elem* __restrict_
     return race_chunk_m<Elem, TPT, kModeResampleOneHot>(logits, q, V, seed, rec, b, c);
   return race_chunk_m<Elem, TPT, kModeBonus>(logits, q, V, seed, rec, b, c);
 }
+
+// Output of one request, by wavefront 0 of the workgroup that raced its last
+// chunk (stream path): reduce the chunk winners, read through coherent loads,
+// and write the output row.  If every residual value rounded to zero
+// (possible only through rounding), race over p at the same row instead.
+template <typename Elem>
+__device__ __forceinline__ void finish_request(const Elem* __restrict__ logits, const int32_t* __restrict__ draft,
+                                               int32_t max_k, int32_t V, int32_t nchunks, uint64_t seed,
+                                               const ReqRecord& rec, int32_t b,
+                                               const unsigned long long* __restrict__ cand,
+                                               int32_t* __restrict__ out, int32_t* __restrict__ num_accepted) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long win = 0ull;
+  for (int32_t c = lane; c < nchunks; c += 64) {
+    const unsigned long long v = load_coherent(cand + (int64_t)b * nchunks + c);
+    win = v > win ? v : win;
+  }
+  win = wave_max(win);
+  if (win == 0ull) {
+    const Elem* lrow = logits + (int64_t)rec.row * V;
+    float bk = 0.f;
+    int32_t bx = INT_MAX;
+    for (int32_t G = lane; G < (V + 3) / 4; G += 64) {
+      float l[4], qz[4];
+      load_group_scalar(lrow, (const float*)nullptr, G, V, l, qz);
+      race_group(l, qz, kModeBonus, -1, rec.c, rec.shift, rec.inv_sum, (uint32_t)seed, (uint32_t)(seed >> 32),
+                 (uint32_t)rec.n, (uint32_t)b, G, bk, bx);
+    }
+    win = wave_max(pack_key(bk, bx));
+  }
+  const int32_t token = unpack_token(win);
+  int32_t* ob = out + (int64_t)b * (max_k + 1);
+  if (lane <= max_k) ob[lane] = lane < rec.n ? draft[rec.slot0 + lane] : (lane == rec.n ? token : -1);
+  if (lane == 0) num_accepted[b] = rec.n;
+}
+
 
 }  // namespace rsv

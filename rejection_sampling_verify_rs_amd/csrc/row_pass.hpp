@@ -25,6 +25,53 @@ struct RowStats {
   double sum;      // random: sum_x exp2(fl32(l_x * c - shift))
 };
 
+// Partials and gathers, plain or through coherent 64-bit accesses (COH: they
+// cross workgroups inside one kernel).
+template <bool COH>
+__device__ __forceinline__ void store_partial(RowPartial* p, float shift, int32_t argmax, double sum) {
+  if (COH) {
+    unsigned long long* w = reinterpret_cast<unsigned long long*>(p);
+    store_coherent(w, ((unsigned long long)(uint32_t)argmax << 32) | __float_as_uint(shift));
+    store_coherent(w + 1, (unsigned long long)__double_as_longlong(sum));
+  } else {
+    RowPartial r;
+    r.shift = shift;
+    r.argmax = argmax;
+    r.sum = sum;
+    *p = r;
+  }
+}
+template <bool COH>
+__device__ __forceinline__ RowPartial load_partial(const RowPartial* p) {
+  if (!COH) return *p;
+  const unsigned long long* w = reinterpret_cast<const unsigned long long*>(p);
+  const unsigned long long a = load_coherent(w), b = load_coherent(w + 1);
+  RowPartial r;
+  r.shift = __uint_as_float((uint32_t)a);
+  r.argmax = (int32_t)(a >> 32);
+  r.sum = __longlong_as_double((long long)b);
+  return r;
+}
+template <bool COH>
+__device__ __forceinline__ void store_gathered(Gathered* g, float lstar, float qstar) {
+  if (COH) {
+    store_coherent(reinterpret_cast<unsigned long long*>(g),
+                   ((unsigned long long)__float_as_uint(qstar) << 32) | __float_as_uint(lstar));
+  } else {
+    g->lstar = lstar;
+    g->qstar = qstar;
+  }
+}
+template <bool COH>
+__device__ __forceinline__ Gathered load_gathered(const Gathered* g) {
+  if (!COH) return *g;
+  const unsigned long long a = load_coherent(reinterpret_cast<const unsigned long long*>(g));
+  Gathered r;
+  r.lstar = __uint_as_float((uint32_t)a);
+  r.qstar = __uint_as_float((uint32_t)(a >> 32));
+  return r;
+}
+
 // Chunk helpers: NV vectors a thread holds (FULL: every vector in range).
 template <typename Elem, int NV, bool FULL>
 __device__ __forceinline__ float chunk_max(const uint4 (&data)[NV], int v0, int tid, int nvec, float m) {
@@ -192,7 +239,7 @@ __device__ __forceinline__ RowStats row_stats(const Elem* __restrict__ prow, int
 // Statistics of chunk c (NV vectors per thread) of logits row `row`,
 // written to partials[row * nsplit + c].  Chunk 0 of a draft position's row
 // also stores l(x*) and q(x*) in *gath (x* = xstar, checked by the caller).
-template <typename Elem, int NV>
+template <typename Elem, int NV, bool COH = false>
 __device__ __forceinline__ void chunk_task(const Elem* __restrict__ logits, const float* __restrict__ q, int64_t row,
                                            float T, int32_t V, int32_t nsplit, int32_t c, int32_t xstar,
                                            int64_t slot, RowPartial* __restrict__ partials,
@@ -238,12 +285,8 @@ __device__ __forceinline__ void chunk_task(const Elem* __restrict__ logits, cons
       extra_idx = head + nvec * W + (tid - 8);
       extra = to_f32(prow[extra_idx]);
     }
-    if (xstar >= 0 && tid == 64) {  // accept-test gathers, off the critical path of the scan
-      Gathered g;
-      g.lstar = to_f32(prow[xstar]);
-      g.qstar = q ? q[slot * V + xstar] : 1.f;
-      gath[slot] = g;
-    }
+    if (xstar >= 0 && tid == 64)  // accept-test gathers, off the critical path of the scan
+      store_gathered<COH>(gath + slot, to_f32(prow[xstar]), q ? q[slot * V + xstar] : 1.f);
   }
 
   // Phase 1: chunk maximum.
@@ -260,13 +303,7 @@ __device__ __forceinline__ void chunk_task(const Elem* __restrict__ logits, cons
       if (extra == m) idx = min(idx, extra_idx);
     }
     idx = block_reduce<kRowThreads>(idx, lds_i, MinOp());
-    if (tid == 0) {
-      RowPartial p;
-      p.shift = m;
-      p.argmax = (idx == INT_MAX) ? -1 : idx;
-      p.sum = 0.0;
-      *out = p;
-    }
+    if (tid == 0) store_partial<COH>(out, m, (idx == INT_MAX) ? -1 : idx, 0.0);
     return;
   }
 
@@ -278,14 +315,11 @@ __device__ __forceinline__ void chunk_task(const Elem* __restrict__ logits, cons
                : chunk_expsum<Elem, NV, false>(data, v0, tid, nvec, cs, shift);
     if (extra_idx != INT_MAX) acc += (double)exp2_hw(fmaf(extra, cs, -shift));
   }
+  // A coherent gather store (issued long ago) is acknowledged before the
+  // workgroup can report its chunk done, which happens after this reduction.
+  if (COH && c == 0 && xstar >= 0 && tid == 64) wait_memory();
   acc = block_reduce<kRowThreads>(acc, lds_d, SumOp());
-  if (tid == 0) {
-    RowPartial p;
-    p.shift = shift;
-    p.argmax = -1;
-    p.sum = acc;
-    *out = p;
-  }
+  if (tid == 0) store_partial<COH>(out, shift, -1, acc);
 }
 
 // Partials merged per batch of independent loads (a row has at most this
@@ -295,12 +329,13 @@ constexpr int kMergeBatch = 8;
 // Merge the nsplit partials of one random row: common shift and fp64 sum.
 // Up to kMergeBatch partials are loaded before any is used, so their
 // latencies overlap.
+template <bool COH = false>
 __device__ __forceinline__ void merge_random(const RowPartial* P, int nsplit, float& shift, double& S) {
   if (nsplit <= kMergeBatch) {
     RowPartial r[kMergeBatch];
 #pragma unroll
     for (int c = 0; c < kMergeBatch; ++c)
-      if (c < nsplit) r[c] = P[c];
+      if (c < nsplit) r[c] = load_partial<COH>(P + c);
     float sh = -INFINITY;
 #pragma unroll
     for (int c = 0; c < kMergeBatch; ++c)
@@ -314,15 +349,18 @@ __device__ __forceinline__ void merge_random(const RowPartial* P, int nsplit, fl
     return;
   }
   float sh = -INFINITY;
-  for (int c = 0; c < nsplit; ++c) sh = fmaxf(sh, P[c].shift);
+  for (int c = 0; c < nsplit; ++c) sh = fmaxf(sh, load_partial<COH>(P + c).shift);
   double acc = 0.0;
-  for (int c = 0; c < nsplit; ++c)
-    if (P[c].sum > 0.0) acc += P[c].sum * exp2((double)P[c].shift - (double)sh);
+  for (int c = 0; c < nsplit; ++c) {
+    const RowPartial r = load_partial<COH>(P + c);
+    if (r.sum > 0.0) acc += r.sum * exp2((double)r.shift - (double)sh);
+  }
   shift = sh;
   S = acc;
 }
 
 // Merge the partials of one greedy row: global max, lowest index holding it.
+template <bool COH = false>
 __device__ __forceinline__ int32_t merge_greedy(const RowPartial* P, int nsplit) {
   float m = -INFINITY;
   int32_t idx = INT_MAX;
@@ -337,12 +375,12 @@ __device__ __forceinline__ int32_t merge_greedy(const RowPartial* P, int nsplit)
     RowPartial r[kMergeBatch];
 #pragma unroll
     for (int c = 0; c < kMergeBatch; ++c)
-      if (c < nsplit) r[c] = P[c];
+      if (c < nsplit) r[c] = load_partial<COH>(P + c);
 #pragma unroll
     for (int c = 0; c < kMergeBatch; ++c)
       if (c < nsplit) take(r[c]);
   } else {
-    for (int c = 0; c < nsplit; ++c) take(P[c]);
+    for (int c = 0; c < nsplit; ++c) take(load_partial<COH>(P + c));
   }
   return idx == INT_MAX ? -1 : idx;
 }

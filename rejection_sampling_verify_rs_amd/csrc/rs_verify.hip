@@ -36,10 +36,13 @@
 #include "row_pass.hpp"
 #include "rs_verify.h"
 #include "scan.hpp"
+#include "stream_path.hpp"
 
 namespace rsv {
 
 constexpr size_t kRegionAlign = 256;
+constexpr int kPathRequest = 1, kPathPhased = 2, kPathStream = 3;
+constexpr int64_t kStreamMinTasksPerPosition = 1024;
 constexpr int kTargetBlocks = 2048;  // enough workgroups to fill 256 CUs several times
 constexpr int kMaxPhases = 4;
 
@@ -172,11 +175,13 @@ struct Plan {
   int row_nv, nsplit;   // this launch
   int race_tpt, race_chunks;
   int race_chunks_max;  // candidate slots per request in the workspace
-  bool per_request;     // one workgroup per request instead of the phased path
+  int path;             // kPathRequest, kPathPhased or kPathStream
   int request_nt;       // threads per per-request workgroup
   int nphases;
   int bounds[kMaxPhases + 1];
-  size_t off_partials, off_gath, off_records, off_cand, total;
+  int stream_lead;      // stream path: positions streamed before races interleave
+  size_t off_partials, off_gath, off_records, off_cand;
+  size_t off_row_count, off_masks, off_state, off_race_count, off_queue, off_tail, off_race_done, total;
 };
 
 static size_t align_up(size_t v) { return (v + kRegionAlign - 1) / kRegionAlign * kRegionAlign; }
@@ -223,7 +228,12 @@ static bool make_plan(int32_t B, int32_t D, int32_t max_k, int32_t V, rs_dtype d
   }
   p.race_chunks = (int)(((int64_t)V + kRaceThreads * p.race_tpt - 1) / (kRaceThreads * p.race_tpt));
   p.race_chunks_max = (int)(((int64_t)V + kRaceThreads * 8 - 1) / (kRaceThreads * 8));
-  p.per_request = force_path == 1 && !(dbg && dbg->probs);
+  if (dbg && dbg->probs)
+    p.path = kPathPhased;  // full probabilities need every row: one phase
+  else if (force_path)
+    p.path = force_path == 1 ? kPathRequest : force_path == 3 ? kPathStream : kPathPhased;
+  else  // the stream path needs enough row tasks per position for decisions to land before later rows start
+    p.path = (int64_t)B * p.nsplit >= kStreamMinTasksPerPosition ? kPathStream : kPathPhased;
   p.request_nt = V >= 65536 ? 1024 : 256;
   // Phases: position ranges [bounds[i], bounds[i+1]).  A request decided in
   // one phase never has the rows of later phases read.  Full probabilities
@@ -247,11 +257,20 @@ static bool make_plan(int32_t B, int32_t D, int32_t max_k, int32_t V, rs_dtype d
     }
   }
   p.bounds[++p.nphases] = L;
+  // Stream path: races interleave with the rows of the last position.
+  p.stream_lead = (ends && ends[0] > 0) ? (ends[0] < L ? ends[0] : L) : (L > 1 ? L - 1 : 1);
   p.off_partials = 0;
   p.off_gath = align_up((size_t)R * p.nsplit_max * sizeof(RowPartial));
   p.off_records = p.off_gath + align_up((size_t)(D > 0 ? D : 1) * sizeof(Gathered));
   p.off_cand = p.off_records + align_up((size_t)B * sizeof(ReqRecord));
-  p.total = p.off_cand + align_up((size_t)B * p.race_chunks_max * sizeof(unsigned long long));
+  p.off_row_count = p.off_cand + align_up((size_t)B * p.race_chunks_max * sizeof(unsigned long long));
+  p.off_masks = p.off_row_count + align_up((size_t)R * sizeof(uint32_t));
+  p.off_state = p.off_masks + align_up((size_t)B * 2 * sizeof(unsigned long long));
+  p.off_race_count = p.off_state + align_up((size_t)B * sizeof(int32_t));
+  p.off_queue = p.off_race_count + align_up((size_t)B * kRaceCountStride * sizeof(uint32_t));
+  p.off_tail = p.off_queue + align_up((size_t)B * sizeof(int32_t));
+  p.off_race_done = p.off_tail + kRegionAlign;
+  p.total = p.off_race_done + align_up((size_t)B * p.race_chunks_max * sizeof(int32_t));
   // 1-D grids must stay below 2^31 workgroups.
   return (int64_t)p.nsplit * L * B + (int64_t)p.race_chunks * B < INT32_MAX;
 }
@@ -314,6 +333,32 @@ static bool dispatch_phase(int nv, int tpt, hipStream_t stream, const Elem* logi
   return false;
 }
 
+template <typename Elem, int NV, int TPT>
+static bool launch_stream_kernels(StreamArgs<Elem>& a, hipStream_t stream, EventLog& evl) {
+  stream_kernel<Elem, NV, TPT><<<(unsigned)a.n_tasks, kRowThreads, 0, stream>>>(a);
+  if (!evl.after_kernel(stream)) return false;
+  if (a.n_race > 0) {
+    stream_race_tail_kernel<Elem, TPT><<<(unsigned)a.n_race, kRaceThreads, 0, stream>>>(a);
+    if (!evl.after_kernel(stream)) return false;
+  }
+  return true;
+}
+
+// 1: launched, 0: a launch failed, -1: no such variant.
+template <typename Elem>
+static int dispatch_stream(int nv, int tpt, StreamArgs<Elem>& a, hipStream_t stream, EventLog& evl) {
+#define RS_STREAM(NV, TPT) \
+  if (nv == NV && tpt == TPT) return launch_stream_kernels<Elem, NV, TPT>(a, stream, evl) ? 1 : 0;
+  RS_STREAM(16, 32)
+  RS_STREAM(16, 8)
+  RS_STREAM(4, 32)
+  RS_STREAM(4, 8)
+  RS_STREAM(1, 32)
+  RS_STREAM(1, 8)
+#undef RS_STREAM
+  return -1;
+}
+
 template <typename Elem>
 static rs_status launch(const void* logits_v, const float* q, const int32_t* draft, const int32_t* cu,
                         const float* temperature, int greedy_all, int32_t B, int32_t D, int32_t max_k, int32_t V,
@@ -329,7 +374,47 @@ static rs_status launch(const void* logits_v, const float* q, const int32_t* dra
   EventLog evl{dbg};
   evl.mark(stream);
 
-  if (p.per_request) {
+  if (p.path == kPathStream) {
+    StreamArgs<Elem> a;
+    a.logits = logits;
+    a.q = q;
+    a.draft = draft;
+    a.cu = cu;
+    a.temperature = temperature;
+    a.seed = seed;
+    a.greedy_all = greedy_all;
+    a.B = B;
+    a.D = D;
+    a.max_k = max_k;
+    a.V = V;
+    a.nsplit = p.nsplit;
+    a.race_chunks = p.race_chunks;
+    a.n_rows = (int64_t)(max_k + 1) * B * p.nsplit;
+    a.n_lead = (int64_t)p.stream_lead * B * p.nsplit;
+    a.n_race = greedy_all ? 0 : (int64_t)B * p.race_chunks;
+    a.n_tasks = a.n_rows + a.n_race;
+    a.partials = partials;
+    a.gath = gath;
+    a.records = records;
+    a.cand = cand;
+    a.row_count = reinterpret_cast<uint32_t*>(w + p.off_row_count);
+    a.masks = reinterpret_cast<unsigned long long*>(w + p.off_masks);
+    a.state = reinterpret_cast<int32_t*>(w + p.off_state);
+    a.race_count = reinterpret_cast<uint32_t*>(w + p.off_race_count);
+    a.queue = reinterpret_cast<int32_t*>(w + p.off_queue);
+    a.tail = reinterpret_cast<uint32_t*>(w + p.off_tail);
+    a.race_done = reinterpret_cast<int32_t*>(w + p.off_race_done);
+    a.out = out;
+    a.nacc = nacc;
+    a.dbg_p = dbg_p;
+    stream_init_kernel<<<(unsigned)B, 64, 0, stream>>>(draft, cu, B, D, max_k, V, a.row_count, a.masks, a.state,
+                                                       a.race_count, a.queue, a.tail, a.race_done, p.race_chunks,
+                                                       out, nacc);
+    if (!evl.after_kernel(stream)) return RS_ERR_HIP;
+    const int launched = dispatch_stream<Elem>(p.row_nv, p.race_tpt, a, stream, evl);
+    if (launched < 0) return RS_ERR_INVALID_ARG;
+    if (launched == 0) return RS_ERR_HIP;
+  } else if (p.path == kPathRequest) {
     if (p.request_nt == 1024)
       request_kernel<Elem, 1024><<<(unsigned)B, 1024, 0, stream>>>(logits, q, draft, cu, temperature, greedy_all, D,
                                                                   max_k, V, seed, out, nacc, dbg_p);
@@ -380,6 +465,7 @@ static rs_status launch(const void* logits_v, const float* q, const int32_t* dra
     }
   }
   if (dbg && dbg->kernels_launched) *dbg->kernels_launched = evl.launched;
+  if (dbg && dbg->path_taken) *dbg->path_taken = p.path;
   return RS_OK;
 }
 
@@ -402,7 +488,7 @@ static rs_status verify_impl(const void* logits, rs_dtype dt, const float* q, co
     const int nv = dbg->row_vectors_per_thread, tpt = dbg->race_tokens_per_thread;
     if (!(nv == 0 || nv == 1 || nv == 4 || nv == 16)) return RS_ERR_INVALID_ARG;
     if (!(tpt == 0 || tpt == 8 || tpt == 32)) return RS_ERR_INVALID_ARG;
-    if (dbg->sampling_path < 0 || dbg->sampling_path > 2) return RS_ERR_INVALID_ARG;
+    if (dbg->sampling_path < 0 || dbg->sampling_path > 3) return RS_ERR_INVALID_ARG;
     if (dbg->num_events < 0 || (dbg->num_events > 0 && !dbg->events)) return RS_ERR_INVALID_ARG;
     if ((dbg->draft_target_prob && !aligned(dbg->draft_target_prob, 8)) || (dbg->probs && !aligned(dbg->probs, 4)))
       return RS_ERR_UNSUPPORTED;

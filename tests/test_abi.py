@@ -126,7 +126,7 @@ def test_debug_knobs_validated(lib):
     d.race_tokens_per_thread = 12
     assert _call(lib, dbg=ctypes.byref(d)) == rs.RS_ERR_INVALID_ARG
     d.race_tokens_per_thread = 0
-    d.sampling_path = 3
+    d.sampling_path = 4
     assert _call(lib, dbg=ctypes.byref(d)) == rs.RS_ERR_INVALID_ARG
     d.sampling_path = 0
     d.num_events = 3  # events array missing

@@ -108,17 +108,18 @@ def test_launch_shapes_give_identical_output():
     ok = ~o.near_tie
     for nv, tpt, path, phases in [(1, 8, 2, (-1,)), (4, 32, 2, (1,)), (16, 8, 2, (3,)), (16, 32, 2, (5,)),
                                   (4, 8, 2, (8,)), (16, 32, 2, (2, 5)), (4, 32, 2, (1, 3, 6)), (16, 32, 1, ()),
-                                  (1, 32, 1, ())]:
+                                  (1, 32, 1, ()), (16, 32, 3, ()), (16, 8, 3, (1,)), (4, 32, 3, (9,)),
+                                  (1, 8, 3, (2,)), (4, 8, 3, (5,))]:
         g = run_gpu(w, row_nv=nv, race_tpt=tpt, path=path, phases=phases)
         np.testing.assert_array_equal(g.tokens[ok], ref.tokens[ok])
         np.testing.assert_array_equal(g.num_accepted[ok], ref.num_accepted[ok])
 
 
 @pytest.mark.parametrize("n", [3, 4, 5])
-@pytest.mark.parametrize("path,phases", [(1, ()), (2, (-1,)), (2, (2,)), (2, (1, 2, 4))])
+@pytest.mark.parametrize("path,phases", [(1, ()), (2, (-1,)), (2, (2,)), (2, (1, 2, 4)), (3, ()), (3, (1,))])
 def test_paths_and_phases_full_size(n, path, phases):
-    """The per-request path, the one-phase split path (every row) and other
-    phase splits all match the oracle at full size."""
+    """The per-request path, the one-phase split path (every row), other
+    phase splits and the stream path all match the oracle at full size."""
     w = W.config(n, device="cuda")
     _say(f"workload {n}: path {path}, phase ends {phases}")
     g = run_gpu(w, path=path, phases=phases, want_p=True)
@@ -133,6 +134,32 @@ def test_rerun_is_bit_identical():
     a, b = run_gpu(w), run_gpu(w)
     np.testing.assert_array_equal(a.tokens, b.tokens)
     np.testing.assert_array_equal(a.num_accepted, b.num_accepted)
+
+
+def test_back_to_back_calls_share_one_workspace():
+    """Calls queued back to back on one stream with one workspace (no host
+    synchronisation between them), alternating inputs and shapes, each give
+    the output of a lone call: the per-call hand-off state (arrival counters,
+    partials, chunk winners, records) never leaks from one call into the next,
+    even from a workspace that starts out as garbage."""
+    dev = torch.device("cuda")
+    ws_ = [W.config(4, device=dev, copy=0), W.config(5, device=dev), W.config(4, device=dev, copy=1)]
+    _say("back-to-back calls: workload 4 copy 0, workload 5, workload 4 copy 1")
+    refs = [run_gpu(w) for w in ws_]
+    for w, r in zip(ws_, refs):
+        compare(r, run_oracle(w), w)
+    size = max(rs.workspace_size(w.B, w.D, w.max_k, w.V, w.logits.dtype) for w in ws_)
+    ws = torch.full((size,), 0xFF, dtype=torch.uint8, device=dev)
+    outs = []
+    for k in range(12):
+        w = ws_[k % 3]
+        out, n = rs.verify(w.logits, w.draft_probs, w.draft_token_ids, w.cu_num_draft_tokens, w.temperature,
+                           seed=w.seed, max_k=w.max_k, workspace=ws)
+        outs.append((k % 3, out, n))
+    torch.cuda.synchronize()
+    for i, out, n in outs:
+        np.testing.assert_array_equal(out.cpu().numpy(), refs[i].tokens)
+        np.testing.assert_array_equal(n.cpu().numpy(), refs[i].num_accepted)
 
 
 # ------------------------------------------------------------- degenerate cases

@@ -181,7 +181,7 @@ struct Plan {
   int bounds[kMaxPhases + 1];
   int stream_lead;      // stream path: positions streamed before races interleave
   size_t off_partials, off_gath, off_records, off_cand;
-  size_t off_row_count, off_masks, off_state, off_race_count, off_queue, off_tail, off_race_done, total;
+  size_t off_row_count, off_masks, off_state, off_race_ctl, off_queue, off_tail, total;
 };
 
 static size_t align_up(size_t v) { return (v + kRegionAlign - 1) / kRegionAlign * kRegionAlign; }
@@ -266,11 +266,10 @@ static bool make_plan(int32_t B, int32_t D, int32_t max_k, int32_t V, rs_dtype d
   p.off_row_count = p.off_cand + align_up((size_t)B * p.race_chunks_max * sizeof(unsigned long long));
   p.off_masks = p.off_row_count + align_up((size_t)R * sizeof(uint32_t));
   p.off_state = p.off_masks + align_up((size_t)B * 2 * sizeof(unsigned long long));
-  p.off_race_count = p.off_state + align_up((size_t)B * sizeof(int32_t));
-  p.off_queue = p.off_race_count + align_up((size_t)B * kRaceCountStride * sizeof(uint32_t));
+  p.off_race_ctl = p.off_state + align_up((size_t)B * sizeof(int32_t));
+  p.off_queue = p.off_race_ctl + align_up((size_t)B * kRaceCtlStride * sizeof(uint32_t));
   p.off_tail = p.off_queue + align_up((size_t)B * sizeof(int32_t));
-  p.off_race_done = p.off_tail + kRegionAlign;
-  p.total = p.off_race_done + align_up((size_t)B * p.race_chunks_max * sizeof(int32_t));
+  p.total = p.off_tail + kRegionAlign;
   // 1-D grids must stay below 2^31 workgroups.
   return (int64_t)p.nsplit * L * B + (int64_t)p.race_chunks * B < INT32_MAX;
 }
@@ -400,16 +399,14 @@ static rs_status launch(const void* logits_v, const float* q, const int32_t* dra
     a.row_count = reinterpret_cast<uint32_t*>(w + p.off_row_count);
     a.masks = reinterpret_cast<unsigned long long*>(w + p.off_masks);
     a.state = reinterpret_cast<int32_t*>(w + p.off_state);
-    a.race_count = reinterpret_cast<uint32_t*>(w + p.off_race_count);
+    a.race_ctl = reinterpret_cast<uint32_t*>(w + p.off_race_ctl);
     a.queue = reinterpret_cast<int32_t*>(w + p.off_queue);
     a.tail = reinterpret_cast<uint32_t*>(w + p.off_tail);
-    a.race_done = reinterpret_cast<int32_t*>(w + p.off_race_done);
     a.out = out;
     a.nacc = nacc;
     a.dbg_p = dbg_p;
     stream_init_kernel<<<(unsigned)B, 64, 0, stream>>>(draft, cu, B, D, max_k, V, a.row_count, a.masks, a.state,
-                                                       a.race_count, a.queue, a.tail, a.race_done, p.race_chunks,
-                                                       out, nacc);
+                                                       a.race_ctl, a.queue, a.tail, out, nacc);
     if (!evl.after_kernel(stream)) return RS_ERR_HIP;
     const int launched = dispatch_stream<Elem>(p.row_nv, p.race_tpt, a, stream, evl);
     if (launched < 0) return RS_ERR_INVALID_ARG;

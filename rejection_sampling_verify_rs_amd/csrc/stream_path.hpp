@@ -1,6 +1,6 @@
 // Stream path: rows, decisions and races in one streaming kernel, with a
-// small kernel before it (per-request set-up) and one after it (races the
-// stream kernel could not run yet).  No workgroup waits on another beyond a
+// small kernel before it (per-request set-up) and one after it (race chunks
+// the stream kernel did not get to).  No workgroup waits on another beyond a
 // short bounded poll.
 //
 // Tasks of the stream kernel, one workgroup each, in launch order: the row
@@ -19,11 +19,18 @@
 // vllm v1 源码精读（五） §7], so those rows cannot change the output.  Rows
 // started before the decision is known are read speculatively.
 //
-// Race tasks take requests in the order they were decided.  A race task whose
-// queue slot is still empty after a short bounded poll leaves its chunk
-// undone; the tail kernel, launched when every request is decided, races every
-// chunk left undone.  The last chunk of a request to be raced, in either
-// kernel, writes its output row.
+// Race work is handed out in chunks through a per-request claim counter, and
+// three kinds of workgroup claim it:
+//   * a row task that finds its request already decided before its position
+//     (and the race record written) races a chunk of that request instead of
+//     leaving: the skipped rows of early-rejecting requests carry most of the
+//     race, overlapped with the row streaming of other requests;
+//   * race tasks (queue slot, chunk), interleaved with the rows of the last
+//     position, take the requests in the order they were decided, after a
+//     short bounded poll of an empty slot;
+//   * the tail kernel, launched when every request is decided, claims every
+//     chunk still unclaimed.
+// The last chunk of a request to be raced writes its output row.
 #pragma once
 
 #include "common.hpp"
@@ -33,10 +40,14 @@
 
 namespace rsv {
 
-constexpr int32_t kStateUndecided = 0;  // per-request state word; decided: 2 + n
+// Per-request state word: undecided, invalid, or decided with n accepted
+// drafts (2 + n), plus kStateReady once a random request's race record is
+// written.
+constexpr int32_t kStateUndecided = 0;
 constexpr int32_t kStateInvalid = 1;
+constexpr int32_t kStateReady = 64;
 constexpr int32_t kQueueSkip = 0x7FFFFFFF;  // queue entry of a request with no race
-constexpr int kRaceCountStride = 16;        // race arrival counters 64 bytes apart
+constexpr int kRaceCtlStride = 32;          // per request: arrivals at [0], claims at [16] (own 64-B lines)
 constexpr int32_t kPollLimit = 32;          // polls of an empty queue slot before leaving the chunk
 
 template <typename Elem>
@@ -57,10 +68,9 @@ struct StreamArgs {
   uint32_t* row_count;        // [R] chunk arrivals per row
   unsigned long long* masks;  // [B][2] accepted / rejected positions
   int32_t* state;             // [B]
-  uint32_t* race_count;       // [B * kRaceCountStride]
+  uint32_t* race_ctl;         // [B * kRaceCtlStride] race chunk arrivals and claims
   int32_t* queue;             // [B] b + 1 or kQueueSkip, in decision order
   uint32_t* tail;             // queue length
-  int32_t* race_done;         // [B * race_chunks] chunk raced by the stream kernel
   int32_t* out;
   int32_t* nacc;
   double* dbg_p;
@@ -123,7 +133,8 @@ __device__ __forceinline__ void stream_decide(const StreamArgs<Elem>& a, int32_t
     r.inv_sum = (float)(1.0 / Sn);
     r.pad[0] = r.pad[1] = r.pad[2] = 0;
     store_record(a.records + b, r);
-    wait_memory();  // the record is visible before the queue entry points to it
+    wait_memory();  // the record is visible before the state or the queue points to it
+    store_coherent32(a.state + b, 2 + n + kStateReady);
     enqueue(a, b + 1);
   }
 }
@@ -189,9 +200,35 @@ __device__ __forceinline__ void stream_row_complete(const StreamArgs<Elem>& a, i
   stream_decide(a, b, n, j, s, K, greedy, cs, shift, S, amax);
 }
 
+// Claim and race one chunk of request b's race (whole workgroup); the last
+// chunk raced writes the output row.  Returns without work once every chunk is
+// claimed.
+template <typename Elem, int TPT>
+__device__ __forceinline__ void stream_race_claim(const StreamArgs<Elem>& a, int32_t b, int32_t* s_word) {
+  const int tid = threadIdx.x;
+  uint32_t* ctl = a.race_ctl + (int64_t)b * kRaceCtlStride;
+  if (tid == 0)
+    *s_word = (int32_t)__hip_atomic_fetch_add(ctl + 16, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int32_t c = *s_word;
+  if (c >= a.race_chunks) return;
+  const ReqRecord rec = load_record(a.records + b);
+  const unsigned long long packed = race_chunk<Elem, TPT>(a.logits, a.q, a.V, a.seed, rec, b, c);
+  if (tid >= 64) return;  // wavefront 0 reports the chunk winner
+  int last = 0;
+  if (tid == 0) {
+    store_coherent(a.cand + (int64_t)b * a.race_chunks + c, packed);
+    wait_memory();
+    last = arrive_last(ctl, (uint32_t)a.race_chunks);
+  }
+  if (__shfl(last, 0))
+    finish_request<Elem>(a.logits, a.draft, a.max_k, a.V, a.race_chunks, a.seed, rec, b, a.cand, a.out, a.nacc);
+}
+
 // Chunk c of row j of request b, unless the request is invalid, has fewer
-// positions or was decided before j.
-template <typename Elem, int NV>
+// positions or was decided before j -- then, once the race record is written,
+// a chunk of its race instead.
+template <typename Elem, int NV, int TPT>
 __device__ __forceinline__ void stream_row_task(const StreamArgs<Elem>& a, int32_t j, int32_t b, int32_t c,
                                                 int32_t* s_word) {
   const int tid = threadIdx.x;
@@ -201,13 +238,17 @@ __device__ __forceinline__ void stream_row_task(const StreamArgs<Elem>& a, int32
   if (tid == 0) *s_word = load_coherent32(a.state + b);
   __syncthreads();
   const int32_t st = *s_word;
+  __syncthreads();  // s_word is reused below
   if (st == kStateInvalid) {  // the task of chunk 0 of position 0 queues it
     if (j == 0 && c == 0 && tid == 0 && a.n_race > 0) enqueue(a, kQueueSkip);
     return;
   }
   const int32_t K = e - s;  // in range: the init kernel validated the request
   if (j > K) return;
-  if (st >= 2 && st - 2 < j) return;  // decided before position j: row not needed
+  if (st >= 2 && ((st - 2) & (kStateReady - 1)) < j) {  // decided before position j: row not needed
+    if (st >= kStateReady) stream_race_claim<Elem, TPT>(a, b, s_word);
+    return;
+  }
   const int32_t xstar = (c == 0 && j < K && T > 0.f) ? a.draft[s + j] : -1;
   const int64_t row = (int64_t)s + b + j;
   chunk_task<Elem, NV, true>(a.logits, a.q, row, T, a.V, a.nsplit, c, xstar, (int64_t)s + j, a.partials, a.gath);
@@ -220,18 +261,15 @@ __device__ __forceinline__ void stream_row_task(const StreamArgs<Elem>& a, int32
   if (__shfl(last, 0)) stream_row_complete(a, b, j, s, K, T);
 }
 
-// Chunk c of the race of queue slot `slot`.  In the stream kernel (tail ==
-// false) an empty slot leaves the chunk to the tail kernel; in the tail kernel
-// every slot is filled and only chunks not yet raced run.
+// Race task of queue slot `slot`: the request decided slot-th.  In the stream
+// kernel (tail == false) an empty slot is polled briefly and then left to the
+// tail kernel, where every slot is filled.
 template <typename Elem, int TPT>
-__device__ __forceinline__ void stream_race_task(const StreamArgs<Elem>& a, int32_t slot, int32_t c, bool tail,
+__device__ __forceinline__ void stream_race_task(const StreamArgs<Elem>& a, int32_t slot, bool tail,
                                                  int32_t* s_word) {
   const int tid = threadIdx.x;
-  int32_t* done = a.race_done + (int64_t)slot * a.race_chunks + c;
   if (tid == 0) {
-    int32_t v = (tail && *done) ? 0 : load_coherent32(a.queue + slot);
-    // A short, bounded poll: the slot may be filled by a row task still in
-    // flight; if it is not, the tail kernel takes the chunk.
+    int32_t v = load_coherent32(a.queue + slot);
     for (int32_t i = 0; !tail && v == 0 && i < kPollLimit; ++i) {
       __builtin_amdgcn_s_sleep(16);
       v = load_coherent32(a.queue + slot);
@@ -240,20 +278,9 @@ __device__ __forceinline__ void stream_race_task(const StreamArgs<Elem>& a, int3
   }
   __syncthreads();
   const int32_t v = *s_word;
-  if (v == 0 || v == kQueueSkip) return;  // empty (left to the tail kernel), raced already, or nothing to race
-  const int32_t b = v - 1;
-  const ReqRecord rec = load_record(a.records + b);
-  const unsigned long long packed = race_chunk<Elem, TPT>(a.logits, a.q, a.V, a.seed, rec, b, c);
-  if (tid >= 64) return;  // wavefront 0 reports the chunk winner
-  int last = 0;
-  if (tid == 0) {
-    if (!tail) *done = 1;  // read by the tail kernel, after this kernel
-    store_coherent(a.cand + (int64_t)b * a.race_chunks + c, packed);
-    wait_memory();
-    last = arrive_last(a.race_count + (int64_t)b * kRaceCountStride, (uint32_t)a.race_chunks);
-  }
-  if (__shfl(last, 0))
-    finish_request<Elem>(a.logits, a.draft, a.max_k, a.V, a.race_chunks, a.seed, rec, b, a.cand, a.out, a.nacc);
+  __syncthreads();  // s_word is reused below
+  if (v == 0 || v == kQueueSkip) return;  // empty (left to the tail kernel) or nothing to race
+  stream_race_claim<Elem, TPT>(a, v - 1, s_word);
 }
 
 template <typename Elem, int NV, int TPT>
@@ -275,24 +302,22 @@ __global__ __launch_bounds__(kRowThreads) void stream_kernel(StreamArgs<Elem> a)
       is_row = rest > both;
     }
     if (!is_row) {
-      stream_race_task<Elem, TPT>(a, (int32_t)(i / a.race_chunks), (int32_t)(i % a.race_chunks), false, &s_word);
+      stream_race_task<Elem, TPT>(a, (int32_t)(i / a.race_chunks), false, &s_word);
       return;
     }
     k = a.n_lead + i;
   }
   const int64_t per_pos = (int64_t)a.B * a.nsplit;
-  stream_row_task<Elem, NV>(a, (int32_t)(k / per_pos), (int32_t)((k / a.nsplit) % a.B), (int32_t)(k % a.nsplit),
-                            &s_word);
+  stream_row_task<Elem, NV, TPT>(a, (int32_t)(k / per_pos), (int32_t)((k / a.nsplit) % a.B),
+                                 (int32_t)(k % a.nsplit), &s_word);
 }
 
-// Every race chunk the stream kernel left undone (one workgroup per
-// (queue slot, chunk)).
+// Every race chunk still unclaimed after the stream kernel (one workgroup per
+// (queue slot, chunk); each claims at most one chunk).
 template <typename Elem, int TPT>
 __global__ __launch_bounds__(kRaceThreads) void stream_race_tail_kernel(StreamArgs<Elem> a) {
   __shared__ int32_t s_word;
-  const int32_t slot = (int32_t)(blockIdx.x / a.race_chunks);
-  const int32_t c = (int32_t)(blockIdx.x % a.race_chunks);
-  stream_race_task<Elem, TPT>(a, slot, c, true, &s_word);
+  stream_race_task<Elem, TPT>(a, (int32_t)(blockIdx.x / a.race_chunks), true, &s_word);
 }
 
 // One wavefront per request: validity, counters, masks, state; -1 row for an
@@ -301,19 +326,15 @@ __global__ __launch_bounds__(64) void stream_init_kernel(const int32_t* __restri
                                                          const int32_t* __restrict__ cu, int32_t B, int32_t D,
                                                          int32_t max_k, int32_t V, uint32_t* __restrict__ row_count,
                                                          unsigned long long* __restrict__ masks,
-                                                         int32_t* __restrict__ state, uint32_t* __restrict__ race_count,
+                                                         int32_t* __restrict__ state, uint32_t* __restrict__ race_ctl,
                                                          int32_t* __restrict__ queue, uint32_t* __restrict__ tail,
-                                                         int32_t* __restrict__ race_done, int32_t race_chunks,
                                                          int32_t* __restrict__ out, int32_t* __restrict__ nacc) {
   const int32_t b = blockIdx.x;
   const int lane = threadIdx.x;
   if (b == 0 && lane == 0) *tail = 0u;
-  if (lane == 0) {
-    queue[b] = 0;
-    race_count[(int64_t)b * kRaceCountStride] = 0u;
-  }
+  if (lane == 0) queue[b] = 0;
+  if (lane < kRaceCtlStride) race_ctl[(int64_t)b * kRaceCtlStride + lane] = 0u;
   if (lane < 2) masks[2 * (int64_t)b + lane] = 0ull;
-  for (int32_t c = lane; c < race_chunks; c += 64) race_done[(int64_t)b * race_chunks + c] = 0;
   const int32_t s = cu[b], e = cu[b + 1];
   bool valid = request_valid(s, e, D, max_k);
   const int32_t K = valid ? e - s : 0;

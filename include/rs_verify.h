@@ -127,7 +127,7 @@ typedef struct rs_debug {
    * the first entry that is 0 or >= max_k + 1 (the last phase always ends at
    * max_k + 1).  At most four phases.  On the stream path phase_ends[0] > 0
    * is the number of positions streamed before race tasks start to
-   * interleave with rows (default max_k). */
+   * interleave with rows (default max_k + 1: all rows first). */
   int32_t phase_ends[3];
   /* HOST pointer or NULL: receives the path the call took (1, 2 or 3). */
   int32_t* path_taken;

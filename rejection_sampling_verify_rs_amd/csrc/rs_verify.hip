@@ -257,8 +257,9 @@ static bool make_plan(int32_t B, int32_t D, int32_t max_k, int32_t V, rs_dtype d
     }
   }
   p.bounds[++p.nphases] = L;
-  // Stream path: races interleave with the rows of the last position.
-  p.stream_lead = (ends && ends[0] > 0) ? (ends[0] < L ? ends[0] : L) : (L > 1 ? L - 1 : 1);
+  // Stream path: by default every row task precedes the race tasks (row
+  // tasks of already-decided requests race in their place meanwhile).
+  p.stream_lead = (ends && ends[0] > 0 && ends[0] < L) ? ends[0] : L;
   p.off_partials = 0;
   p.off_gath = align_up((size_t)R * p.nsplit_max * sizeof(RowPartial));
   p.off_records = p.off_gath + align_up((size_t)(D > 0 ? D : 1) * sizeof(Gathered));

@@ -29,7 +29,8 @@ FLAG_ACCEPT_TIE = 1
 FLAG_RACE_TIE = 2
 FLAG_ZERO_RESIDUAL = 4
 FLAG_INVALID = 8
-NEAR_TIE_FLAGS = FLAG_ACCEPT_TIE | FLAG_RACE_TIE | FLAG_ZERO_RESIDUAL
+FLAG_TOPP_TIE = 16
+NEAR_TIE_FLAGS = FLAG_ACCEPT_TIE | FLAG_RACE_TIE | FLAG_ZERO_RESIDUAL | FLAG_TOPP_TIE
 
 DEFAULT_EPS = 1e-6
 
@@ -57,6 +58,11 @@ def _load():
     i32, i64, u64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_double
     lib.rso_verify.argtypes = [P, i32, P, P, P, P, i32, i32, i32, i32, u64, i32, f64, P, P, P, P, i32]
     lib.rso_verify.restype = ctypes.c_int
+    lib.rso_verify_filtered.argtypes = [P, i32, P, P, P, P, P, P, i32, i32, i32, i32, u64, i32, f64, P, P, P, P,
+                                        i32]
+    lib.rso_verify_filtered.restype = ctypes.c_int
+    lib.rso_filtered_probs_row.argtypes = [P, i32, f64, i32, f64, f64, P, P, P]
+    lib.rso_filtered_probs_row.restype = None
     lib.rso_probs.argtypes = [P, i32, P, P, i32, i32, P]
     lib.rso_probs.restype = ctypes.c_int
     lib.rso_softmax_row.argtypes = [P, i32, f64, P]
@@ -116,8 +122,10 @@ class OracleResult:
 
 def verify(logits, draft_probs, draft_token_ids, cu_num_draft_tokens, temperature, seed: int,
            max_k: int, *, greedy_only: bool = False, eps: float = DEFAULT_EPS,
-           threads: int = 0) -> OracleResult:
-    """Run the oracle on one batch (see rs_oracle.c, rso_verify)."""
+           threads: int = 0, top_k=None, top_p=None) -> OracleResult:
+    """Run the oracle on one batch (see rs_oracle.c, rso_verify_filtered).
+    top_k [B] int32 / top_p [B] float32 (or None) filter the target
+    distribution of random requests."""
     lib = _load()
     lg, code = _logits_arg(logits)
     V = int(lg.shape[-1])
@@ -131,13 +139,17 @@ def verify(logits, draft_probs, draft_token_ids, cu_num_draft_tokens, temperatur
         raise ValueError(f"logits hold {lg.size} values, expected (D + B) * V = {(D + B) * V}")
     if q is not None and q.size != D * V:
         raise ValueError("draft_probs must be [D, V]")
+    tk = None if top_k is None else _to_numpy(top_k, np.int32)
+    tp = None if top_p is None else _to_numpy(top_p, np.float32)
+    if (tk is not None and tk.size != B) or (tp is not None and tp.size != B):
+        raise ValueError("top_k / top_p must have B entries")
     out = np.empty((B, max_k + 1), np.int32)
     nacc = np.empty(B, np.int32)
     flags = np.empty(B, np.int32)
     pd = np.empty(D, np.float64)
-    rc = lib.rso_verify(_ptr(lg), code, _ptr(q), _ptr(ids), _ptr(cu), _ptr(T), B, D, max_k, V,
-                        int(seed) & ((1 << 64) - 1), int(greedy_only), float(eps), _ptr(out),
-                        _ptr(nacc), _ptr(flags), _ptr(pd), int(threads))
+    rc = lib.rso_verify_filtered(_ptr(lg), code, _ptr(q), _ptr(ids), _ptr(cu), _ptr(T), _ptr(tk), _ptr(tp),
+                                 B, D, max_k, V, int(seed) & ((1 << 64) - 1), int(greedy_only), float(eps),
+                                 _ptr(out), _ptr(nacc), _ptr(flags), _ptr(pd), int(threads))
     if rc != 0:
         raise RuntimeError("oracle rejected its arguments")
     return OracleResult(out, nacc, flags, pd)
@@ -170,6 +182,20 @@ def softmax_row(l: np.ndarray, T: float) -> np.ndarray:
     p = np.empty_like(l)
     lib.rso_softmax_row(_ptr(l), int(l.shape[0]), float(T), _ptr(p))
     return p
+
+
+def filtered_probs_row(l: np.ndarray, T: float, top_k: int = 0, top_p: float = 1.0,
+                       eps: float = DEFAULT_EPS):
+    """Target distribution p' of one row after temperature, top-k and top-p
+    (rso_filtered_probs_row).  Returns (p' [V] fp64, near_tie)."""
+    lib = _load()
+    l = np.ascontiguousarray(l, dtype=np.float64)
+    p = np.empty_like(l)
+    scratch = np.empty_like(l)
+    tie = ctypes.c_int(0)
+    lib.rso_filtered_probs_row(_ptr(l), int(l.shape[0]), float(T), int(top_k), float(top_p), float(eps), _ptr(p),
+                               _ptr(scratch), ctypes.byref(tie))
+    return p, bool(tie.value)
 
 
 def philox(ctr, key) -> np.ndarray:

@@ -41,6 +41,23 @@
  *    so n + 1 tokens are emitted.  [Ch.12 §12.3.4; "投机解码端到端深挖"
  *    §8 (accept_lens = num_correct_drafts + 1)]
  *
+ *  - Optional top-k / top-p filtering of the target distribution, applied
+ *    after the temperature and before the accept test, the residual and the
+ *    bonus: rejection sampling constrains the target distribution with
+ *    temperature, top-k and top-p (not min_p or penalties).
+ *      [Ch.12 §12.2.3 (last sentences); §12.9, top-k / top-p bullet:
+ *       batch-level top_k / top_p expanded to tokens, then applied in
+ *       compute_probs]
+ *    The pages name the step but not its tie rules; the reading taken:
+ *      top-k keeps token x iff fewer than k tokens have a strictly larger
+ *      logit (ties at the k-th value are all kept); k <= 0 or k >= V is off.
+ *      top-p (after top-k) keeps x iff the probability mass, under the
+ *      top-k-filtered softmax, of the tokens with a strictly larger logit is
+ *      below top_p (tokens of equal logit are kept or dropped together; the
+ *      largest logit is always kept); top_p outside (0, 1) is off.
+ *      p' = softmax restricted to the kept tokens.  Greedy requests ignore
+ *      both.
+ *
  * Readings where the pages leave a step open (each is also listed in the
  * design notes):
  *  - Random stream: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
@@ -62,6 +79,9 @@
  *   race:         lower bound of the winner's key <= upper bound of any
  *                 other key, the bounds taken with p -> p(1 -/+ eps) and
  *                 E -> E(1 +/- eps).
+ *   top-p:        for some group of equal logits, the mass of the larger
+ *                 kept tokens is within eps * top_p * S_k of top_p * S_k
+ *                 (S_k = the top-k-filtered mass) on a sampled or tested row.
  *
  * Arithmetic: inputs are widened exactly (bf16 -> fp32 -> fp64; temperature
  * from fp32) and everything is computed in fp64 with the C library's exp/log.
@@ -83,6 +103,7 @@
 #define RSO_FLAG_RACE_TIE 2
 #define RSO_FLAG_ZERO_RESIDUAL 4
 #define RSO_FLAG_INVALID 8
+#define RSO_FLAG_TOPP_TIE 16
 
 /* ------------------------------------------------------------------------ */
 /* Philox4x32-10.  One round maps (c0, c1, c2, c3) with key (k0, k1) to
@@ -177,6 +198,71 @@ static int32_t argmax_lowest(const double* l, int32_t V) {
   return best;
 }
 
+static int cmp_desc(const void* a, const void* b) {
+  double x = *(const double*)a, y = *(const double*)b;
+  return (x < y) - (x > y);
+}
+
+/* Target distribution p' of one row with top-k / top-p filtering:
+ *   M = max_y l_y / T;  w_x = exp(l_x / T - M);
+ *   top-k: kept iff l_x >= v_k, v_k = the k-th largest logit (k-th entry of
+ *          the logits sorted in descending order), so exactly the tokens with
+ *          fewer than k strictly larger logits;
+ *   top-p: walk the kept logits in descending order in groups of equal value;
+ *          a group stays iff the mass of the groups before it is below
+ *          top_p * S_k, S_k = sum of w over the top-k-kept tokens;
+ *   p'_x = w_x / sum of w over the kept tokens (0 for dropped tokens).
+ * k <= 0 or k >= V disables top-k; top_p outside (0, 1) disables top-p.
+ * *near_tie is set when some group's preceding mass is within
+ * eps * top_p * S_k of top_p * S_k.  sorted is scratch of length V. */
+void rso_filtered_probs_row(const double* l, int32_t V, double T, int32_t k, double top_p, double eps,
+                            double* p, double* sorted, int* near_tie) {
+  *near_tie = 0;
+  double M = -INFINITY;
+  for (int32_t x = 0; x < V; ++x) {
+    double s = l[x] / T;
+    if (s > M) M = s;
+  }
+  double vk = -INFINITY; /* keep l >= vk */
+  if (k > 0 && k < V) {
+    memcpy(sorted, l, sizeof(double) * (size_t)V);
+    qsort(sorted, (size_t)V, sizeof(double), cmp_desc);
+    vk = sorted[k - 1];
+  }
+  double Sk = 0.0;
+  for (int32_t x = 0; x < V; ++x) {
+    p[x] = (l[x] >= vk) ? exp(l[x] / T - M) : 0.0;
+    Sk += p[x];
+  }
+  double vp = -INFINITY;
+  if (top_p > 0.0 && top_p < 1.0) {
+    int32_t n = 0;
+    for (int32_t x = 0; x < V; ++x)
+      if (l[x] >= vk) sorted[n++] = l[x];
+    qsort(sorted, (size_t)n, sizeof(double), cmp_desc);
+    double target = top_p * Sk, before = 0.0;
+    int32_t i = 0;
+    while (i < n) {
+      double v = sorted[i];
+      if (fabs(before - target) <= eps * target) *near_tie = 1;
+      if (!(before < target)) break;
+      vp = v;
+      double group = 0.0;
+      while (i < n && sorted[i] == v) {
+        group += exp(v / T - M);
+        ++i;
+      }
+      before += group;
+    }
+  }
+  double S = 0.0;
+  for (int32_t x = 0; x < V; ++x) {
+    if (l[x] < vp) p[x] = 0.0;
+    S += p[x];
+  }
+  for (int32_t x = 0; x < V; ++x) p[x] /= S;
+}
+
 static void load_row(const void* logits, int dtype, int64_t row, int32_t V, double* l) {
   for (int32_t x = 0; x < V; ++x) l[x] = widen(logits, dtype, row * (int64_t)V + x);
 }
@@ -221,12 +307,15 @@ static int32_t race(const double* r, const double* rlo, const double* rhi, int32
  *   T        [B] temperatures; T <= 0 marks a greedy request.
  *   greedy_only: treat every request as greedy (T and q ignored).
  *   out      [B, max_k+1] tokens (-1 padded); num_accepted [B]; flags [B].
+ *   top_k    [B] or NULL, top_p [B] or NULL: per-request filtering of the
+ *            target distribution (see rso_filtered_probs_row).
  *   p_draft  [D] or NULL: p(x*) at each evaluated random position, NaN elsewhere.
  * Returns 0, or -1 on an argument error. */
-int rso_verify(const void* logits, int32_t dtype, const float* q, const int32_t* draft,
-               const int32_t* cu, const float* T, int32_t B, int32_t D, int32_t max_k, int32_t V,
-               uint64_t seed, int32_t greedy_only, double eps, int32_t* out, int32_t* num_accepted,
-               int32_t* flags, double* p_draft, int32_t nthreads) {
+int rso_verify_filtered(const void* logits, int32_t dtype, const float* q, const int32_t* draft,
+                        const int32_t* cu, const float* T, const int32_t* top_k, const float* top_p,
+                        int32_t B, int32_t D, int32_t max_k, int32_t V, uint64_t seed, int32_t greedy_only,
+                        double eps, int32_t* out, int32_t* num_accepted, int32_t* flags, double* p_draft,
+                        int32_t nthreads) {
   if (!logits || !draft || !cu || !out || !num_accepted || !flags) return -1;
   if (!greedy_only && !T) return -1;
   if (B < 0 || D < 0 || V < 1 || max_k < 0 || (dtype != RSO_F32 && dtype != RSO_BF16)) return -1;
@@ -246,7 +335,8 @@ int rso_verify(const void* logits, int32_t dtype, const float* q, const int32_t*
     double* rlo = (double*)malloc(sizeof(double) * (size_t)V);
     double* rhi = (double*)malloc(sizeof(double) * (size_t)V);
     double* E = (double*)malloc(sizeof(double) * (size_t)V);
-    if (!l || !p || !r || !rlo || !rhi || !E) {
+    double* srt = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!l || !p || !r || !rlo || !rhi || !E || !srt) {
 #pragma omp atomic write
       failed = 1;
     }
@@ -282,9 +372,13 @@ int rso_verify(const void* logits, int32_t dtype, const float* q, const int32_t*
         token = argmax_lowest(l, V);
       } else {
         double Tb = (double)T[b];
+        int32_t kb = top_k ? top_k[b] : 0;
+        double pb = top_p ? (double)top_p[b] : 1.0;
+        int ptie = 0;
         for (int32_t j = 0; j < K; ++j) {
           load_row(logits, dtype, row0 + j, V, l);
-          rso_softmax_row(l, V, Tb, p);
+          rso_filtered_probs_row(l, V, Tb, kb, pb, eps, p, srt, &ptie);
+          if (ptie) flags[b] |= RSO_FLAG_TOPP_TIE;
           int32_t xs = draft[s + j];
           double qs = q ? (double)q[(int64_t)(s + j) * V + xs] : 1.0;
           double u = rso_accept_uniform(seed, b, j);
@@ -298,7 +392,8 @@ int rso_verify(const void* logits, int32_t dtype, const float* q, const int32_t*
         }
         /* p at the sampled position n (bonus row when n == K) */
         load_row(logits, dtype, row0 + n, V, l);
-        rso_softmax_row(l, V, Tb, p);
+        rso_filtered_probs_row(l, V, Tb, kb, pb, eps, p, srt, &ptie);
+        if (ptie) flags[b] |= RSO_FLAG_TOPP_TIE;
         if (n < K) {
           int32_t xs = draft[s + n];
           for (int32_t x = 0; x < V; ++x) {
@@ -338,9 +433,18 @@ int rso_verify(const void* logits, int32_t dtype, const float* q, const int32_t*
       ob[n] = token;
       num_accepted[b] = n;
     }
-    free(l); free(p); free(r); free(rlo); free(rhi); free(E);
+    free(l); free(p); free(r); free(rlo); free(rhi); free(E); free(srt);
   }
   return failed ? -1 : 0;
+}
+
+/* rso_verify_filtered with no top-k / top-p. */
+int rso_verify(const void* logits, int32_t dtype, const float* q, const int32_t* draft,
+               const int32_t* cu, const float* T, int32_t B, int32_t D, int32_t max_k, int32_t V,
+               uint64_t seed, int32_t greedy_only, double eps, int32_t* out, int32_t* num_accepted,
+               int32_t* flags, double* p_draft, int32_t nthreads) {
+  return rso_verify_filtered(logits, dtype, q, draft, cu, T, NULL, NULL, B, D, max_k, V, seed, greedy_only,
+                             eps, out, num_accepted, flags, p_draft, nthreads);
 }
 
 /* Full p = softmax(l / T_b) for every row of every request (rows of greedy

@@ -158,6 +158,35 @@ rs_status rs_verify(const void* target_logits, rs_dtype logits_dtype, const floa
                     int32_t* num_accepted, void* workspace, size_t workspace_bytes,
                     const rs_debug* debug, hipStream_t stream);
 
+/* rs_verify with top-k / top-p filtering of each random request's target
+ * distribution before the accept test, the residual and the bonus: the
+ * rejection sampler constrains the target distribution with temperature,
+ * top-k and top-p [第12章 §12.2.3; §12.9 (compute_probs applies the
+ * per-request top_k / top_p to every draft position)].  The pages do not print
+ * the tie rules; the library's reading:
+ *   top-k keeps token x iff fewer than top_k[b] tokens have a strictly larger
+ *     logit (every token tied with the k-th largest stays);
+ *   top-p then keeps x iff the probability mass, under the top-k-filtered
+ *     softmax at temperature T_b, of the tokens with a strictly larger logit
+ *     is below top_p[b] (tokens of equal logit stay or go together; the
+ *     largest logit always stays);
+ *   p' = the softmax restricted to the kept tokens.
+ *   top_k        [B] int32 device, or NULL; top_k[b] <= 0 or >= V: no top-k
+ *   top_p        [B] fp32 device, or NULL; top_p[b] outside (0, 1): no top-p
+ * Greedy requests (T <= 0) ignore both.  Every other argument, the layout,
+ * ownership, workspace size (rs_verify_workspace_size) and error rules are
+ * those of rs_verify; additionally V must be below 2^20 when top_k or top_p
+ * is given (RS_ERR_UNSUPPORTED otherwise).  Filtered calls run the phased
+ * path: one 1024-thread workgroup per needed row finds the row's threshold
+ * by radix selection before the accept tests. */
+rs_status rs_verify_filtered(const void* target_logits, rs_dtype logits_dtype, const float* draft_probs,
+                             const int32_t* draft_token_ids, const int32_t* cu_num_draft_tokens,
+                             const float* temperature, const int32_t* top_k, const float* top_p,
+                             int32_t batch, int32_t total_draft_tokens, int32_t max_k, int32_t vocab,
+                             uint64_t seed, int32_t* output_token_ids, int32_t* num_accepted,
+                             void* workspace, size_t workspace_bytes, const rs_debug* debug,
+                             hipStream_t stream);
+
 /* Greedy argmax-match for every request (no temperature, q or random numbers)
  * [第12章 §12.2.4; 投机解码（Speculative Decoding）端到端深挖 §7.1 path A].
  * Same layout, ownership and error rules as rs_verify. */

@@ -65,6 +65,9 @@ def load_library(path: str = LIB_PATH):
     lib.rs_verify_workspace_size.restype = sz
     lib.rs_verify.argtypes = [P, ctypes.c_int, P, P, P, P, i32, i32, i32, i32, u64, P, P, P, sz, P, P]
     lib.rs_verify.restype = ctypes.c_int
+    lib.rs_verify_filtered.argtypes = [P, ctypes.c_int, P, P, P, P, P, P, i32, i32, i32, i32, u64, P, P, P, sz, P,
+                                       P]
+    lib.rs_verify_filtered.restype = ctypes.c_int
     lib.rs_verify_greedy.argtypes = [P, ctypes.c_int, P, P, i32, i32, i32, i32, P, P, P, sz, P]
     lib.rs_verify_greedy.restype = ctypes.c_int
     lib.rs_status_string.argtypes = [ctypes.c_int]
@@ -181,8 +184,13 @@ def verify(target_logits: torch.Tensor, draft_probs: Optional[torch.Tensor], dra
            cu_num_draft_tokens: torch.Tensor, temperature: torch.Tensor, *, seed: int, max_k: int,
            out: Optional[torch.Tensor] = None, num_accepted: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None, debug: Optional[Debug] = None,
-           stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Batched verify (rs_verify).  Returns (output_token_ids [B, max_k+1], num_accepted [B])."""
+           stream: Optional[torch.cuda.Stream] = None, top_k: Optional[torch.Tensor] = None,
+           top_p: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Batched verify.  Returns (output_token_ids [B, max_k+1], num_accepted [B]).
+
+    With top_k ([B] int32) and / or top_p ([B] float32) it calls
+    rs_verify_filtered (target distribution filtered per request), else
+    rs_verify."""
     lib = load_library()
     dev, B, D, V, out, num_accepted, workspace, stream = _common(
         target_logits, draft_token_ids, cu_num_draft_tokens, max_k, out, num_accepted, workspace, stream)
@@ -193,16 +201,25 @@ def verify(target_logits: torch.Tensor, draft_probs: Optional[torch.Tensor], dra
         _dev_tensor(draft_probs, "draft_probs", torch.float32, dev)
         if draft_probs.numel() != D * V:
             raise ValueError("draft_probs must be [D, V]")
+    for t, name, dt in ((top_k, "top_k", torch.int32), (top_p, "top_p", torch.float32)):
+        if t is not None:
+            _dev_tensor(t, name, dt, dev)
+            if t.numel() != B:
+                raise ValueError(f"{name} must have B entries")
     dbg, keep = (None, None)
     if debug is not None:
         dbg, keep = debug._struct(stream)
-    status = lib.rs_verify(
-        target_logits.data_ptr(), _DTYPE[target_logits.dtype],
-        draft_probs.data_ptr() if draft_probs is not None else None,
-        draft_token_ids.data_ptr() if D > 0 else None, cu_num_draft_tokens.data_ptr(), temperature.data_ptr(),
-        B, D, int(max_k), V, int(seed) & ((1 << 64) - 1), out.data_ptr(), num_accepted.data_ptr(),
-        workspace.data_ptr(), workspace.numel(), ctypes.byref(dbg) if dbg is not None else None,
-        ctypes.c_void_p(stream.cuda_stream))
+    head = (target_logits.data_ptr(), _DTYPE[target_logits.dtype],
+            draft_probs.data_ptr() if draft_probs is not None else None,
+            draft_token_ids.data_ptr() if D > 0 else None, cu_num_draft_tokens.data_ptr(), temperature.data_ptr())
+    tail = (B, D, int(max_k), V, int(seed) & ((1 << 64) - 1), out.data_ptr(), num_accepted.data_ptr(),
+            workspace.data_ptr(), workspace.numel(), ctypes.byref(dbg) if dbg is not None else None,
+            ctypes.c_void_p(stream.cuda_stream))
+    if top_k is None and top_p is None:
+        status = lib.rs_verify(*head, *tail)
+    else:
+        status = lib.rs_verify_filtered(*head, top_k.data_ptr() if top_k is not None else None,
+                                        top_p.data_ptr() if top_p is not None else None, *tail)
     if debug is not None:
         debug.kernels_launched = int(keep[0].value)
         debug.path_taken = int(keep[1].value)

@@ -51,7 +51,8 @@ struct ReqRecord {
   float c;          // log2(e) / T
   float shift;      // merged shift of the sampled row
   float inv_sum;    // 1 / sum of the sampled row, rounded to fp32
-  int32_t pad[3];
+  float tau;        // tokens with logit < tau are filtered out (-inf: none)
+  int32_t pad[2];
 };
 static_assert(sizeof(ReqRecord) == 48, "ReqRecord layout");
 

@@ -37,15 +37,17 @@ __device__ __forceinline__ float race_weight(float ex, float qv, int32_t x, int3
 // probabilities qv[] (tokens at or beyond V carry l = -inf, so r = 0).  Keeps
 // the thread's best (key, x); tokens arrive in increasing x, so '>' keeps the
 // lowest index among equal keys.
-template <int MODE>
+template <int MODE, bool FILT>
 __device__ __forceinline__ void race_group_m(const float (&l)[4], const float (&qv)[4], int32_t exclude, float cs,
-                                             float shift, float inv_sum, uint32_t k0, uint32_t k1, uint32_t j,
-                                             uint32_t b, int32_t G, float& best_key, int32_t& best_x) {
+                                             float shift, float inv_sum, float tau, uint32_t k0, uint32_t k1,
+                                             uint32_t j, uint32_t b, int32_t G, float& best_key, int32_t& best_x) {
   const PhiloxOut o = philox4x32_10((uint32_t)G, j, b, 1u, k0, k1);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int32_t x = 4 * G + k;
-    const float r = race_weight<MODE>(exp2_hw(fmaf(l[k], cs, -shift)), qv[k], x, exclude, inv_sum);
+    // a token below the filter threshold has p' = 0 (exp2(-inf) = 0)
+    const float lk = FILT ? (l[k] >= tau ? l[k] : -INFINITY) : l[k];
+    const float r = race_weight<MODE>(exp2_hw(fmaf(lk, cs, -shift)), qv[k], x, exclude, inv_sum);
     const float key = r * __builtin_amdgcn_rcpf(-__builtin_amdgcn_logf(race_uniform_f32(o.w[k])));
     const bool up = key > best_key;
     best_key = up ? key : best_key;
@@ -53,16 +55,27 @@ __device__ __forceinline__ void race_group_m(const float (&l)[4], const float (&
   }
 }
 
-// The same with the mode chosen at run time (per-request path, output fallback).
+// The same with the mode and the filter chosen at run time (per-request path,
+// output fallback); tau = -inf means no filter.
 __device__ __forceinline__ void race_group(const float (&l)[4], const float (&qv)[4], int mode, int32_t exclude,
-                                           float cs, float shift, float inv_sum, uint32_t k0, uint32_t k1,
+                                           float cs, float shift, float inv_sum, float tau, uint32_t k0, uint32_t k1,
                                            uint32_t j, uint32_t b, int32_t G, float& best_key, int32_t& best_x) {
-  if (mode == kModeResampleQ)
-    race_group_m<kModeResampleQ>(l, qv, exclude, cs, shift, inv_sum, k0, k1, j, b, G, best_key, best_x);
-  else if (mode == kModeResampleOneHot)
-    race_group_m<kModeResampleOneHot>(l, qv, exclude, cs, shift, inv_sum, k0, k1, j, b, G, best_key, best_x);
-  else
-    race_group_m<kModeBonus>(l, qv, exclude, cs, shift, inv_sum, k0, k1, j, b, G, best_key, best_x);
+  if (tau > -INFINITY) {
+    if (mode == kModeResampleQ)
+      race_group_m<kModeResampleQ, true>(l, qv, exclude, cs, shift, inv_sum, tau, k0, k1, j, b, G, best_key, best_x);
+    else if (mode == kModeResampleOneHot)
+      race_group_m<kModeResampleOneHot, true>(l, qv, exclude, cs, shift, inv_sum, tau, k0, k1, j, b, G, best_key,
+                                              best_x);
+    else
+      race_group_m<kModeBonus, true>(l, qv, exclude, cs, shift, inv_sum, tau, k0, k1, j, b, G, best_key, best_x);
+  } else if (mode == kModeResampleQ) {
+    race_group_m<kModeResampleQ, false>(l, qv, exclude, cs, shift, inv_sum, tau, k0, k1, j, b, G, best_key, best_x);
+  } else if (mode == kModeResampleOneHot) {
+    race_group_m<kModeResampleOneHot, false>(l, qv, exclude, cs, shift, inv_sum, tau, k0, k1, j, b, G, best_key,
+                                             best_x);
+  } else {
+    race_group_m<kModeBonus, false>(l, qv, exclude, cs, shift, inv_sum, tau, k0, k1, j, b, G, best_key, best_x);
+  }
 }
 
 // Element-wise load of group G (tokens at or beyond V get l = -inf, q = 0).
@@ -80,10 +93,10 @@ __device__ __forceinline__ void load_group_scalar(const Elem* __restrict__ lrow,
 // Groups G0 + tid + i * kRaceThreads (i < TPT / 4) of one row.  FULL: every
 // group lies below Gfull (vector-loadable), so loads and arithmetic run
 // unguarded and the loads can be waited on one at a time.
-template <typename Elem, int TPT, int MODE, bool FULL>
+template <typename Elem, int TPT, int MODE, bool FILT, bool FULL>
 __device__ __forceinline__ void race_span(const Elem* __restrict__ lrow, const float* __restrict__ qrow, int32_t V,
                                           int32_t G0, int32_t Gfull, int32_t Gend, int32_t exclude, float cs,
-                                          float shift, float inv_sum, uint32_t k0, uint32_t k1, uint32_t j,
+                                          float shift, float inv_sum, float tau, uint32_t k0, uint32_t k1, uint32_t j,
                                           uint32_t b, float& best_key, int32_t& best_x) {
   constexpr int NG = TPT / 4;
   constexpr bool kQ = MODE == kModeResampleQ;
@@ -117,11 +130,11 @@ __device__ __forceinline__ void race_span(const Elem* __restrict__ lrow, const f
     } else {
       continue;
     }
-    race_group_m<MODE>(l, qv, exclude, cs, shift, inv_sum, k0, k1, j, b, G, best_key, best_x);
+    race_group_m<MODE, FILT>(l, qv, exclude, cs, shift, inv_sum, tau, k0, k1, j, b, G, best_key, best_x);
   }
 }
 
-template <typename Elem, int TPT, int MODE>
+template <typename Elem, int TPT, int MODE, bool FILT>
 __device__ __forceinline__ unsigned long long race_chunk_m(const Elem* __restrict__ logits,
                                                            const float* __restrict__ q, int32_t V, uint64_t seed,
                                                            const ReqRecord& rec, int32_t b, int32_t c) {
@@ -139,11 +152,13 @@ __device__ __forceinline__ unsigned long long race_chunk_m(const Elem* __restric
   float best_key = 0.f;
   int32_t best_x = INT_MAX;
   if (G0 + kRaceThreads * NG <= Gfull)
-    race_span<Elem, TPT, MODE, true>(lrow, qrow, V, G0, Gfull, Gend, rec.exclude, rec.c, rec.shift, rec.inv_sum, k0,
-                                     k1, (uint32_t)rec.n, (uint32_t)b, best_key, best_x);
+    race_span<Elem, TPT, MODE, FILT, true>(lrow, qrow, V, G0, Gfull, Gend, rec.exclude, rec.c, rec.shift,
+                                           rec.inv_sum, rec.tau, k0, k1, (uint32_t)rec.n, (uint32_t)b, best_key,
+                                           best_x);
   else
-    race_span<Elem, TPT, MODE, false>(lrow, qrow, V, G0, Gfull, Gend, rec.exclude, rec.c, rec.shift, rec.inv_sum,
-                                      k0, k1, (uint32_t)rec.n, (uint32_t)b, best_key, best_x);
+    race_span<Elem, TPT, MODE, FILT, false>(lrow, qrow, V, G0, Gfull, Gend, rec.exclude, rec.c, rec.shift,
+                                            rec.inv_sum, rec.tau, k0, k1, (uint32_t)rec.n, (uint32_t)b, best_key,
+                                            best_x);
   return block_reduce<kRaceThreads>(pack_key(best_key, best_x), lds_u, MaxOp());
 }
 
@@ -154,10 +169,17 @@ template <typename Elem, int TPT>
 __device__ __forceinline__ unsigned long long race_chunk(const Elem* __restrict__ logits, const float* __restrict__ q,
                                                          int32_t V, uint64_t seed, const ReqRecord& rec, int32_t b,
                                                          int32_t c) {
-  if (rec.mode == kModeResampleQ) return race_chunk_m<Elem, TPT, kModeResampleQ>(logits, q, V, seed, rec, b, c);
+  if (rec.tau > -INFINITY) {  // filtered target distribution (top-k / top-p)
+    if (rec.mode == kModeResampleQ)
+      return race_chunk_m<Elem, TPT, kModeResampleQ, true>(logits, q, V, seed, rec, b, c);
+    if (rec.mode == kModeResampleOneHot)
+      return race_chunk_m<Elem, TPT, kModeResampleOneHot, true>(logits, q, V, seed, rec, b, c);
+    return race_chunk_m<Elem, TPT, kModeBonus, true>(logits, q, V, seed, rec, b, c);
+  }
+  if (rec.mode == kModeResampleQ) return race_chunk_m<Elem, TPT, kModeResampleQ, false>(logits, q, V, seed, rec, b, c);
   if (rec.mode == kModeResampleOneHot)
-    return race_chunk_m<Elem, TPT, kModeResampleOneHot>(logits, q, V, seed, rec, b, c);
-  return race_chunk_m<Elem, TPT, kModeBonus>(logits, q, V, seed, rec, b, c);
+    return race_chunk_m<Elem, TPT, kModeResampleOneHot, false>(logits, q, V, seed, rec, b, c);
+  return race_chunk_m<Elem, TPT, kModeBonus, false>(logits, q, V, seed, rec, b, c);
 }
 
 // Output of one request, by wavefront 0 of the workgroup that raced its last
@@ -184,7 +206,7 @@ __device__ __forceinline__ void finish_request(const Elem* __restrict__ logits, 
     for (int32_t G = lane; G < (V + 3) / 4; G += 64) {
       float l[4], qz[4];
       load_group_scalar(lrow, (const float*)nullptr, G, V, l, qz);
-      race_group(l, qz, kModeBonus, -1, rec.c, rec.shift, rec.inv_sum, (uint32_t)seed, (uint32_t)(seed >> 32),
+      race_group(l, qz, kModeBonus, -1, rec.c, rec.shift, rec.inv_sum, rec.tau, (uint32_t)seed, (uint32_t)(seed >> 32),
                  (uint32_t)rec.n, (uint32_t)b, G, bk, bx);
     }
     win = wave_max(pack_key(bk, bx));

@@ -63,7 +63,7 @@ __device__ __forceinline__ unsigned long long race_row(const Elem* __restrict__ 
         } else {
           load_group_scalar(lrow, qrow, G, V, l, qv);
         }
-        race_group(l, qv, mode, exclude, cs, shift, inv_sum, k0, k1, j, b, G, best_key, best_x);
+        race_group(l, qv, mode, exclude, cs, shift, inv_sum, -INFINITY, k0, k1, j, b, G, best_key, best_x);
       }
     }
   };

@@ -30,6 +30,7 @@
 #include <stdint.h>
 
 #include "common.hpp"
+#include "filter.hpp"
 #include "philox.hpp"
 #include "race.hpp"
 #include "request_path.hpp"
@@ -56,7 +57,8 @@ __global__ __launch_bounds__(kRowThreads) void phase_kernel(
     const int32_t* __restrict__ cu, const float* __restrict__ temperature, int32_t greedy_all, int32_t D,
     int32_t max_k, int32_t V, uint64_t seed, int32_t j_begin, int32_t j_count, int32_t nsplit, int32_t n_row,
     int32_t race_chunks, int32_t n_race, int32_t race_phase, RowPartial* __restrict__ partials,
-    Gathered* __restrict__ gath, const ReqRecord* __restrict__ records, unsigned long long* __restrict__ cand) {
+    Gathered* __restrict__ gath, const ReqRecord* __restrict__ records, unsigned long long* __restrict__ cand,
+    const int32_t* __restrict__ top_k, const float* __restrict__ top_p) {
   const int32_t id = blockIdx.x;
   const int32_t both = min(n_row, n_race);
   int32_t t;
@@ -77,6 +79,7 @@ __global__ __launch_bounds__(kRowThreads) void phase_kernel(
     if (!request_valid(s, e, D, max_k) || j > e - s) return;
     if (j_begin > 0 && records[b].mode != kModeActive) return;
     const float T = greedy_all ? 0.f : temperature[b];
+    if (T > 0.f && filter_on(top_k, top_p, b, V)) return;  // the filter kernel took this row
     int32_t xstar = -1;
     if (c == 0 && j < e - s && T > 0.f) {
       xstar = draft[s + j];
@@ -100,9 +103,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const float* __restrict__ temperature, int32_t greedy_all, int32_t D, int32_t max_k, int32_t V, int32_t nsplit,
     uint64_t seed, const RowPartial* __restrict__ partials, const Gathered* __restrict__ gath, int32_t j_begin,
     int32_t j_end, int32_t phase, ReqRecord* __restrict__ records, int32_t* __restrict__ out,
-    int32_t* __restrict__ num_accepted, double* __restrict__ dbg_p) {
+    int32_t* __restrict__ num_accepted, double* __restrict__ dbg_p, const int32_t* __restrict__ top_k,
+    const float* __restrict__ top_p, const FilterRec* __restrict__ frec) {
   scan_phase<Elem>(blockIdx.x, q, draft, cu, temperature, greedy_all, D, max_k, V, nsplit, seed, partials, gath,
-                   j_begin, j_end, phase, records, out, num_accepted, dbg_p);
+                   j_begin, j_end, phase, records, out, num_accepted, dbg_p, top_k, top_p, frec);
 }
 
 // ------------------------------------------------------------- emit kernel
@@ -133,7 +137,7 @@ __global__ __launch_bounds__(64) void emit_kernel(const Elem* __restrict__ logit
     for (int32_t G = lane; G < (V + 3) / 4; G += 64) {
       float l[4], qz[4];
       load_group_scalar(lrow, (const float*)nullptr, G, V, l, qz);
-      race_group(l, qz, kModeBonus, -1, rec.c, rec.shift, rec.inv_sum, (uint32_t)seed, (uint32_t)(seed >> 32),
+      race_group(l, qz, kModeBonus, -1, rec.c, rec.shift, rec.inv_sum, rec.tau, (uint32_t)seed, (uint32_t)(seed >> 32),
                  (uint32_t)rec.n, (uint32_t)b, G, bk, bx);
     }
     win = wave_max(pack_key(bk, bx));
@@ -145,13 +149,15 @@ __global__ __launch_bounds__(64) void emit_kernel(const Elem* __restrict__ logit
 }
 
 // -------------------------------------------------- debug: full p per row
-// p in the fp32 form the race uses, for every row of every random request
-// (every row is streamed: the call runs one phase).
+// p (p' with top-k / top-p) in the fp32 form the race uses, for every row of
+// every random request (every row is streamed: the call runs one phase).
 template <typename Elem>
 __global__ __launch_bounds__(256) void probs_kernel(const Elem* __restrict__ logits, const int32_t* __restrict__ cu,
                                                     const float* __restrict__ temperature, int32_t D, int32_t max_k,
                                                     int32_t V, int32_t nsplit, const RowPartial* __restrict__ partials,
-                                                    float* __restrict__ probs) {
+                                                    float* __restrict__ probs, const int32_t* __restrict__ top_k,
+                                                    const float* __restrict__ top_p,
+                                                    const FilterRec* __restrict__ frec) {
   const int32_t j = blockIdx.x % (max_k + 1);
   const int32_t b = blockIdx.x / (max_k + 1);
   const int32_t s = cu[b], e = cu[b + 1];
@@ -160,12 +166,21 @@ __global__ __launch_bounds__(256) void probs_kernel(const Elem* __restrict__ log
   if (!(T > 0.f)) return;
   const float cs = scale_of(T);
   const int64_t row = (int64_t)s + b + j;
-  float shift;
+  float shift, tau = -INFINITY;
   double S;
-  merge_random(partials + row * nsplit, nsplit, shift, S);
+  if (filter_on(top_k, top_p, b, V)) {
+    const FilterRec f = frec[row];
+    shift = f.shift;
+    S = f.sum;
+    tau = f.tau;
+  } else {
+    merge_random(partials + row * nsplit, nsplit, shift, S);
+  }
   const float inv = (float)(1.0 / S);
-  for (int32_t x = threadIdx.x; x < V; x += 256)
-    probs[row * V + x] = exp2_hw(fmaf(to_f32(logits[row * V + x]), cs, -shift)) * inv;
+  for (int32_t x = threadIdx.x; x < V; x += 256) {
+    const float l = to_f32(logits[row * V + x]);
+    probs[row * V + x] = l >= tau ? exp2_hw(fmaf(l, cs, -shift)) * inv : 0.f;
+  }
 }
 
 // ---------------------------------------------------------------- host side
@@ -181,7 +196,7 @@ struct Plan {
   int bounds[kMaxPhases + 1];
   int stream_lead;      // stream path: positions streamed before races interleave
   size_t off_partials, off_gath, off_records, off_cand;
-  size_t off_row_count, off_masks, off_state, off_race_ctl, off_queue, off_tail, total;
+  size_t off_row_count, off_masks, off_state, off_race_ctl, off_queue, off_tail, off_frec, total;
 };
 
 static size_t align_up(size_t v) { return (v + kRegionAlign - 1) / kRegionAlign * kRegionAlign; }
@@ -200,7 +215,8 @@ static int auto_phase_end(int L, int k) {
 }
 
 // Sizes are assumed validated (B >= 1, V >= 1, 0 <= max_k <= 32, 0 <= D <= B * max_k).
-static bool make_plan(int32_t B, int32_t D, int32_t max_k, int32_t V, rs_dtype dt, const rs_debug* dbg, Plan& p) {
+static bool make_plan(int32_t B, int32_t D, int32_t max_k, int32_t V, rs_dtype dt, const rs_debug* dbg,
+                      bool filtered, Plan& p) {
   const int force_nv = dbg ? dbg->row_vectors_per_thread : 0;
   const int force_tpt = dbg ? dbg->race_tokens_per_thread : 0;
   const int force_path = dbg ? dbg->sampling_path : 0;
@@ -228,8 +244,8 @@ static bool make_plan(int32_t B, int32_t D, int32_t max_k, int32_t V, rs_dtype d
   }
   p.race_chunks = (int)(((int64_t)V + kRaceThreads * p.race_tpt - 1) / (kRaceThreads * p.race_tpt));
   p.race_chunks_max = (int)(((int64_t)V + kRaceThreads * 8 - 1) / (kRaceThreads * 8));
-  if (dbg && dbg->probs)
-    p.path = kPathPhased;  // full probabilities need every row: one phase
+  if ((dbg && dbg->probs) || filtered)
+    p.path = kPathPhased;  // full probabilities need every row (one phase); filters run per phase
   else if (force_path)
     p.path = force_path == 1 ? kPathRequest : force_path == 3 ? kPathStream : kPathPhased;
   else  // the stream path needs enough row tasks per position for decisions to land before later rows start
@@ -270,7 +286,8 @@ static bool make_plan(int32_t B, int32_t D, int32_t max_k, int32_t V, rs_dtype d
   p.off_race_ctl = p.off_state + align_up((size_t)B * sizeof(int32_t));
   p.off_queue = p.off_race_ctl + align_up((size_t)B * kRaceCtlStride * sizeof(uint32_t));
   p.off_tail = p.off_queue + align_up((size_t)B * sizeof(int32_t));
-  p.total = p.off_tail + kRegionAlign;
+  p.off_frec = p.off_tail + kRegionAlign;
+  p.total = p.off_frec + align_up((size_t)R * sizeof(FilterRec));
   // 1-D grids must stay below 2^31 workgroups.
   return (int64_t)p.nsplit * L * B + (int64_t)p.race_chunks * B < INT32_MAX;
 }
@@ -306,21 +323,23 @@ template <typename Elem, int NV, int TPT>
 static void launch_phase(hipStream_t stream, const Elem* logits, const float* q, const int32_t* draft,
                          const int32_t* cu, const float* temperature, int greedy_all, int32_t D, int32_t max_k,
                          int32_t V, uint64_t seed, const PhaseArgs& a, RowPartial* partials, Gathered* gath,
-                         const ReqRecord* records, unsigned long long* cand) {
+                         const ReqRecord* records, unsigned long long* cand, const int32_t* top_k,
+                         const float* top_p) {
   phase_kernel<Elem, NV, TPT><<<(unsigned)(a.n_row + a.n_race), kRowThreads, 0, stream>>>(
       logits, q, draft, cu, temperature, greedy_all, D, max_k, V, seed, a.j_begin, a.j_count, a.nsplit, a.n_row,
-      a.race_chunks, a.n_race, a.race_phase, partials, gath, records, cand);
+      a.race_chunks, a.n_race, a.race_phase, partials, gath, records, cand, top_k, top_p);
 }
 
 template <typename Elem>
 static bool dispatch_phase(int nv, int tpt, hipStream_t stream, const Elem* logits, const float* q,
                            const int32_t* draft, const int32_t* cu, const float* temperature, int greedy_all,
                            int32_t D, int32_t max_k, int32_t V, uint64_t seed, const PhaseArgs& a,
-                           RowPartial* partials, Gathered* gath, const ReqRecord* records, unsigned long long* cand) {
+                           RowPartial* partials, Gathered* gath, const ReqRecord* records, unsigned long long* cand,
+                           const int32_t* top_k, const float* top_p) {
 #define RS_PHASE(NV, TPT)                                                                                           \
   if (nv == NV && tpt == TPT) {                                                                                     \
     launch_phase<Elem, NV, TPT>(stream, logits, q, draft, cu, temperature, greedy_all, D, max_k, V, seed, a,        \
-                                partials, gath, records, cand);                                                     \
+                                partials, gath, records, cand, top_k, top_p);                                       \
     return true;                                                                                                    \
   }
   RS_PHASE(16, 32)
@@ -361,15 +380,17 @@ static int dispatch_stream(int nv, int tpt, StreamArgs<Elem>& a, hipStream_t str
 
 template <typename Elem>
 static rs_status launch(const void* logits_v, const float* q, const int32_t* draft, const int32_t* cu,
-                        const float* temperature, int greedy_all, int32_t B, int32_t D, int32_t max_k, int32_t V,
-                        uint64_t seed, int32_t* out, int32_t* nacc, void* ws, const Plan& p, const rs_debug* dbg,
-                        hipStream_t stream) {
+                        const float* temperature, const int32_t* top_k, const float* top_p, int greedy_all, int32_t B,
+                        int32_t D, int32_t max_k, int32_t V, uint64_t seed, int32_t* out, int32_t* nacc, void* ws,
+                        const Plan& p, const rs_debug* dbg, hipStream_t stream) {
   const Elem* logits = static_cast<const Elem*>(logits_v);
   char* w = static_cast<char*>(ws);
   RowPartial* partials = reinterpret_cast<RowPartial*>(w + p.off_partials);
   Gathered* gath = reinterpret_cast<Gathered*>(w + p.off_gath);
   ReqRecord* records = reinterpret_cast<ReqRecord*>(w + p.off_records);
   unsigned long long* cand = reinterpret_cast<unsigned long long*>(w + p.off_cand);
+  FilterRec* frec = reinterpret_cast<FilterRec*>(w + p.off_frec);
+  const bool filtered = !greedy_all && (top_k || top_p);
   double* dbg_p = dbg ? dbg->draft_target_prob : nullptr;
   EventLog evl{dbg};
   evl.mark(stream);
@@ -430,18 +451,24 @@ static rs_status launch(const void* logits_v, const float* q, const int32_t* dra
       a.race_chunks = p.race_chunks;
       a.n_race = (ph >= 2 && !greedy_all) ? p.race_chunks * B : 0;
       a.race_phase = ph - 1;
+      if (filtered) {  // thresholds and kept mass of the filtered requests' rows of this phase
+        filter_kernel<Elem><<<(unsigned)(a.j_count * B), kFilterThreads, 0, stream>>>(
+            logits, q, draft, cu, temperature, top_k, top_p, D, max_k, V, a.j_begin, a.j_count, records, frec, gath);
+        if (!evl.after_kernel(stream)) return RS_ERR_HIP;
+      }
       if (!dispatch_phase<Elem>(p.row_nv, p.race_tpt, stream, logits, q, draft, cu, temperature, greedy_all, D,
-                                max_k, V, seed, a, partials, gath, records, cand))
+                                max_k, V, seed, a, partials, gath, records, cand, top_k, top_p))
         return RS_ERR_INVALID_ARG;
       if (!evl.after_kernel(stream)) return RS_ERR_HIP;
       if (dbg && dbg->probs && !greedy_all) {
-        probs_kernel<Elem><<<(unsigned)((max_k + 1) * B), 256, 0, stream>>>(logits, cu, temperature, D, max_k, V,
-                                                                              p.nsplit, partials, dbg->probs);
+        probs_kernel<Elem><<<(unsigned)((max_k + 1) * B), 256, 0, stream>>>(
+            logits, cu, temperature, D, max_k, V, p.nsplit, partials, dbg->probs, top_k, top_p, frec);
         if (!evl.after_kernel(stream)) return RS_ERR_HIP;
       }
       scan_kernel<Elem><<<(unsigned)B, kScanThreads, 0, stream>>>(q, draft, cu, temperature, greedy_all, D, max_k, V,
                                                                   p.nsplit, seed, partials, gath, a.j_begin,
-                                                                  p.bounds[ph], ph, records, out, nacc, dbg_p);
+                                                                  p.bounds[ph], ph, records, out, nacc, dbg_p, top_k,
+                                                                  top_p, frec);
       if (!evl.after_kernel(stream)) return RS_ERR_HIP;
     }
     if (!greedy_all) {  // race of the requests decided in the last phase, then the output rows
@@ -454,7 +481,7 @@ static rs_status launch(const void* logits_v, const float* q, const int32_t* dra
       a.n_race = p.race_chunks * B;
       a.race_phase = p.nphases;
       if (!dispatch_phase<Elem>(p.row_nv, p.race_tpt, stream, logits, q, draft, cu, temperature, greedy_all, D,
-                                max_k, V, seed, a, partials, gath, records, cand))
+                                max_k, V, seed, a, partials, gath, records, cand, top_k, top_p))
         return RS_ERR_INVALID_ARG;
       if (!evl.after_kernel(stream)) return RS_ERR_HIP;
       emit_kernel<Elem><<<(unsigned)B, 64, 0, stream>>>(logits, draft, max_k, V, p.race_chunks, seed, records, cand,
@@ -468,9 +495,9 @@ static rs_status launch(const void* logits_v, const float* q, const int32_t* dra
 }
 
 static rs_status verify_impl(const void* logits, rs_dtype dt, const float* q, const int32_t* draft, const int32_t* cu,
-                             const float* temperature, int greedy_all, int32_t B, int32_t D, int32_t max_k, int32_t V,
-                             uint64_t seed, int32_t* out, int32_t* nacc, void* ws, size_t ws_bytes,
-                             const rs_debug* dbg, hipStream_t stream) {
+                             const float* temperature, const int32_t* top_k, const float* top_p, int greedy_all,
+                             int32_t B, int32_t D, int32_t max_k, int32_t V, uint64_t seed, int32_t* out,
+                             int32_t* nacc, void* ws, size_t ws_bytes, const rs_debug* dbg, hipStream_t stream) {
   // Every check below runs before the first HIP call.
   if (B < 0 || D < 0 || V < 1 || max_k < 0) return RS_ERR_INVALID_ARG;
   if (dt != RS_F32 && dt != RS_BF16) return RS_ERR_UNSUPPORTED;
@@ -480,8 +507,11 @@ static rs_status verify_impl(const void* logits, rs_dtype dt, const float* q, co
     return RS_ERR_INVALID_ARG;
   const size_t es = dt == RS_BF16 ? 2 : 4;
   if (!aligned(logits, es) || (q && !aligned(q, 4)) || !aligned(cu, 4) || !aligned(out, 4) || !aligned(nacc, 4) ||
-      (draft && !aligned(draft, 4)) || (temperature && !aligned(temperature, 4)))
+      (draft && !aligned(draft, 4)) || (temperature && !aligned(temperature, 4)) || (top_k && !aligned(top_k, 4)) ||
+      (top_p && !aligned(top_p, 4)))
     return RS_ERR_UNSUPPORTED;
+  // fixed-point masses of the top-p selection stay below 2^64 for V < 2^20
+  if ((top_k || top_p) && V >= (1 << 20)) return RS_ERR_UNSUPPORTED;
   if (dbg) {
     const int nv = dbg->row_vectors_per_thread, tpt = dbg->race_tokens_per_thread;
     if (!(nv == 0 || nv == 1 || nv == 4 || nv == 16)) return RS_ERR_INVALID_ARG;
@@ -492,13 +522,13 @@ static rs_status verify_impl(const void* logits, rs_dtype dt, const float* q, co
       return RS_ERR_UNSUPPORTED;
   }
   Plan p;
-  if (!make_plan(B, D, max_k, V, dt, dbg, p)) return RS_ERR_UNSUPPORTED;
+  if (!make_plan(B, D, max_k, V, dt, dbg, !greedy_all && (top_k || top_p), p)) return RS_ERR_UNSUPPORTED;
   if (!ws || !aligned(ws, 16) || ws_bytes < p.total) return RS_ERR_WORKSPACE;
   if (dt == RS_BF16)
-    return launch<uint16_t>(logits, q, draft, cu, temperature, greedy_all, B, D, max_k, V, seed, out, nacc, ws, p, dbg,
-                            stream);
-  return launch<float>(logits, q, draft, cu, temperature, greedy_all, B, D, max_k, V, seed, out, nacc, ws, p, dbg,
-                       stream);
+    return launch<uint16_t>(logits, q, draft, cu, temperature, top_k, top_p, greedy_all, B, D, max_k, V, seed, out,
+                            nacc, ws, p, dbg, stream);
+  return launch<float>(logits, q, draft, cu, temperature, top_k, top_p, greedy_all, B, D, max_k, V, seed, out, nacc,
+                       ws, p, dbg, stream);
 }
 
 }  // namespace rsv
@@ -511,7 +541,7 @@ size_t rs_verify_workspace_size(int32_t batch, int32_t total_draft_tokens, int32
   if (batch == 0 && total_draft_tokens == 0 && vocab >= 1 && max_k >= 0 && max_k <= RS_MAX_SPEC_LEN) return 0;
   if (!rsv::sizes_ok(batch, total_draft_tokens, max_k, vocab)) return 0;
   rsv::Plan p;
-  if (!rsv::make_plan(batch, total_draft_tokens, max_k, vocab, logits_dtype, nullptr, p)) return 0;
+  if (!rsv::make_plan(batch, total_draft_tokens, max_k, vocab, logits_dtype, nullptr, false, p)) return 0;
   return p.total;
 }
 
@@ -521,17 +551,28 @@ rs_status rs_verify(const void* target_logits, rs_dtype logits_dtype, const floa
                     int32_t* output_token_ids, int32_t* num_accepted, void* workspace, size_t workspace_bytes,
                     const rs_debug* debug, hipStream_t stream) {
   return rsv::verify_impl(target_logits, logits_dtype, draft_probs, draft_token_ids, cu_num_draft_tokens, temperature,
-                          0, batch, total_draft_tokens, max_k, vocab, seed, output_token_ids, num_accepted, workspace,
-                          workspace_bytes, debug, stream);
+                          nullptr, nullptr, 0, batch, total_draft_tokens, max_k, vocab, seed, output_token_ids,
+                          num_accepted, workspace, workspace_bytes, debug, stream);
+}
+
+rs_status rs_verify_filtered(const void* target_logits, rs_dtype logits_dtype, const float* draft_probs,
+                             const int32_t* draft_token_ids, const int32_t* cu_num_draft_tokens,
+                             const float* temperature, const int32_t* top_k, const float* top_p, int32_t batch,
+                             int32_t total_draft_tokens, int32_t max_k, int32_t vocab, uint64_t seed,
+                             int32_t* output_token_ids, int32_t* num_accepted, void* workspace,
+                             size_t workspace_bytes, const rs_debug* debug, hipStream_t stream) {
+  return rsv::verify_impl(target_logits, logits_dtype, draft_probs, draft_token_ids, cu_num_draft_tokens, temperature,
+                          top_k, top_p, 0, batch, total_draft_tokens, max_k, vocab, seed, output_token_ids,
+                          num_accepted, workspace, workspace_bytes, debug, stream);
 }
 
 rs_status rs_verify_greedy(const void* target_logits, rs_dtype logits_dtype, const int32_t* draft_token_ids,
                            const int32_t* cu_num_draft_tokens, int32_t batch, int32_t total_draft_tokens,
                            int32_t max_k, int32_t vocab, int32_t* output_token_ids, int32_t* num_accepted,
                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return rsv::verify_impl(target_logits, logits_dtype, nullptr, draft_token_ids, cu_num_draft_tokens, nullptr, 1,
-                          batch, total_draft_tokens, max_k, vocab, 0, output_token_ids, num_accepted, workspace,
-                          workspace_bytes, nullptr, stream);
+  return rsv::verify_impl(target_logits, logits_dtype, nullptr, draft_token_ids, cu_num_draft_tokens, nullptr,
+                          nullptr, nullptr, 1, batch, total_draft_tokens, max_k, vocab, 0, output_token_ids,
+                          num_accepted, workspace, workspace_bytes, nullptr, stream);
 }
 
 const char* rs_status_string(rs_status status) {

@@ -8,6 +8,9 @@
 //  - greedy requests accept iff x* == argmax [§12.2.4; 端到端深挖 §7.1].
 //  - the first rejected position n ends the request: later drafts are
 //    discarded [§12.9; vllm v1 源码精读（五） §7]; a ballot finds it.
+//  - a request with top-k / top-p takes shift, sum and the threshold tau of
+//    each row from the filter kernel's record: p'(x*) = 0 when l(x*) < tau
+//    [§12.2.3; §12.9 (compute_probs)].
 //  - if no position of the phase rejects and the bonus row K lies in it,
 //    n = K (bonus) [§12.3.2]; otherwise the request stays active for the
 //    next phase.
@@ -16,6 +19,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "filter.hpp"
 #include "philox.hpp"
 #include "row_pass.hpp"
 
@@ -27,7 +31,8 @@ __device__ __forceinline__ void scan_phase(
     const float* __restrict__ temperature, int32_t greedy_all, int32_t D, int32_t max_k, int32_t V, int32_t nsplit,
     uint64_t seed, const RowPartial* __restrict__ partials, const Gathered* __restrict__ gath, int32_t j_begin,
     int32_t j_end, int32_t phase, ReqRecord* __restrict__ records, int32_t* __restrict__ out,
-    int32_t* __restrict__ num_accepted, double* __restrict__ dbg_p) {
+    int32_t* __restrict__ num_accepted, double* __restrict__ dbg_p, const int32_t* __restrict__ top_k,
+    const float* __restrict__ top_p, const FilterRec* __restrict__ frec) {
   const int lane = threadIdx.x & 63;
   // Loads are grouped by what their addresses depend on (b, then cu[b]) so
   // each group's latencies overlap.
@@ -50,7 +55,8 @@ __device__ __forceinline__ void scan_phase(
   const bool in_phase = j < j_end && j <= K;
   // Phase 1 reads every draft id (lane = position) to validate the request.
   const int32_t x = (j < K && (in_phase || j_begin == 0)) ? draft[s + j] : -1;
-  float shift = -INFINITY;
+  const bool filt = !greedy && filter_on(top_k, top_p, b, V);
+  float shift = -INFINITY, tau = -INFINITY;
   double S = 0.0;
   int32_t amax = -1;
   double ps = __builtin_nan("");
@@ -64,9 +70,16 @@ __device__ __forceinline__ void scan_phase(
     } else {
       const double u = j < K ? accept_uniform(seed, b, j) : 0.0;
       const Gathered g = j < K ? gath[s + j] : Gathered{0.f, 0.f};
-      merge_random(P, nsplit, shift, S);
+      if (filt) {  // p' from the row's filter record; p'(x*) = 0 below the threshold
+        const FilterRec f = frec[row];
+        shift = f.shift;
+        S = f.sum;
+        tau = f.tau;
+      } else {
+        merge_random(P, nsplit, shift, S);
+      }
       if (j < K) {
-        ps = exp2((double)g.lstar * (double)cs - (double)shift) / S;
+        ps = g.lstar >= tau ? exp2((double)g.lstar * (double)cs - (double)shift) / S : 0.0;
         accept = u * (double)g.qstar < ps;
       }
     }
@@ -92,6 +105,7 @@ __device__ __forceinline__ void scan_phase(
   }
   const int src = n - j_begin;
   const float shift_n = __shfl(shift, src);
+  const float tau_n = __shfl(tau, src);
   const double S_n = __shfl(S, src);
   const int32_t amax_n = __shfl(amax, src);
   const int32_t x_n = __shfl(x, src);
@@ -115,7 +129,8 @@ __device__ __forceinline__ void scan_phase(
     r.c = cs;
     r.shift = shift_n;
     r.inv_sum = (float)(1.0 / S_n);
-    r.pad[0] = r.pad[1] = r.pad[2] = 0;
+    r.tau = tau_n;
+    r.pad[0] = r.pad[1] = 0;
     records[b] = r;
   }
 }

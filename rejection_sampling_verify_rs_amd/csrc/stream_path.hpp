@@ -131,7 +131,8 @@ __device__ __forceinline__ void stream_decide(const StreamArgs<Elem>& a, int32_t
     r.c = cs;
     r.shift = sh;
     r.inv_sum = (float)(1.0 / Sn);
-    r.pad[0] = r.pad[1] = r.pad[2] = 0;
+    r.tau = -INFINITY;
+    r.pad[0] = r.pad[1] = 0;
     store_record(a.records + b, r);
     wait_memory();  // the record is visible before the state or the queue points to it
     store_coherent32(a.state + b, 2 + n + kStateReady);

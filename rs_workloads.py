@@ -24,7 +24,10 @@ Value recipes follow the five workloads the verify step is measured on:
  5. B=512, K=3,  V=129280, bf16 ~N(0, 4^2); sigma_b ~ U[0.1, 2.0] per request;
                             q = softmax(l + N(0, sigma_b^2)); T = 1.0; all random
 
-Draft ids are sampled from q wherever q is given.  All randomness comes from a
+Draft ids are sampled from q wherever q is given.  Any workload can carry
+per-request top-k / top-p settings (Workload.with_filters); the filtered
+benchmark variant is workload 4 with top_k = 50 and top_p = 0.9 for every
+request.  All randomness comes from a
 torch.Generator seeded with 1000 + the workload number (plus a copy index for
 the benchmark's rotating input copies) on the device the inputs are built on,
 so CPU-built and GPU-built inputs of one workload are statistically alike but
@@ -56,6 +59,8 @@ class Workload:
     temperature: torch.Tensor            # [B] fp32; <= 0 marks a greedy request
     seed: int
     num_draft: List[int] = field(default_factory=list)
+    top_k: Optional[torch.Tensor] = None  # [B] int32 or None (no top-k)
+    top_p: Optional[torch.Tensor] = None  # [B] fp32 or None (no top-p)
 
     @property
     def B(self) -> int:
@@ -81,7 +86,26 @@ class Workload:
         mv = lambda t: None if t is None else t.to(device)
         return Workload(self.name, mv(self.logits), mv(self.draft_probs), mv(self.draft_token_ids),
                         mv(self.cu_num_draft_tokens), mv(self.temperature), self.seed,
-                        list(self.num_draft))
+                        list(self.num_draft), mv(self.top_k), mv(self.top_p))
+
+    def with_filters(self, top_k=None, top_p=None, name: Optional[str] = None) -> "Workload":
+        """The same batch with per-request top-k / top-p settings: each of
+        top_k / top_p is None, a scalar for every request, or a length-B
+        sequence."""
+        def expand(v, dtype):
+            if v is None:
+                return None
+            if isinstance(v, (int, float)):
+                return torch.full((self.B,), v, dtype=dtype, device=self.device)
+            t = torch.as_tensor(v, dtype=dtype).to(self.device)
+            assert t.shape == (self.B,)
+            return t.contiguous()
+        w = self.to(self.device)
+        w.top_k = expand(top_k, torch.int32)
+        w.top_p = expand(top_p, torch.float32)
+        if name:
+            w.name = name
+        return w
 
 
 def _gen(device, seed: int) -> torch.Generator:

@@ -46,7 +46,7 @@ def run_gpu(w: W.Workload, *, greedy_entry: bool = False, want_p: bool = False, 
         if want_probs:
             dbg.probs = torch.full((w.D + w.B, w.V), float("nan"), dtype=torch.float32, device=dev)
     out, n = rs.verify(w.logits, w.draft_probs, w.draft_token_ids, w.cu_num_draft_tokens, w.temperature,
-                       seed=w.seed, max_k=w.max_k, debug=dbg)
+                       seed=w.seed, max_k=w.max_k, debug=dbg, top_k=w.top_k, top_p=w.top_p)
     torch.cuda.synchronize()
     r = GpuResult(out.cpu().numpy(), n.cpu().numpy())
     if want_p:
@@ -61,7 +61,7 @@ def run_oracle(w: W.Workload, *, greedy_entry: bool = False) -> oracle.OracleRes
     if greedy_entry:
         return oracle.verify_greedy(w.logits, w.draft_token_ids, w.cu_num_draft_tokens, w.max_k)
     return oracle.verify(w.logits, w.draft_probs, w.draft_token_ids, w.cu_num_draft_tokens, w.temperature,
-                         w.seed, w.max_k)
+                         w.seed, w.max_k, top_k=w.top_k, top_p=w.top_p)
 
 
 def compare(g: GpuResult, o: oracle.OracleResult, w: W.Workload, *, max_flag_frac: Optional[float] = None) -> dict:

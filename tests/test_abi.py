@@ -27,8 +27,8 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["rs_abi_version", "rs_status_string", "rs_verify", "rs_verify_greedy",
-                                     "rs_verify_workspace_size"]
+    assert _declared_functions() == ["rs_abi_version", "rs_status_string", "rs_verify", "rs_verify_filtered",
+                                     "rs_verify_greedy", "rs_verify_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -157,3 +157,31 @@ def test_python_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         rs.verify(x, None, torch.zeros(2, dtype=torch.int32), torch.tensor([0, 2], dtype=torch.int32),
                   torch.ones(1), seed=0, max_k=2)
+
+
+def _call_filtered(lib, **kw):
+    a = dict(logits=DUMMY, dtype=1, q=None, draft=DUMMY, cu=DUMMY, T=DUMMY, top_k=DUMMY, top_p=DUMMY, B=2, D=4,
+             max_k=2, V=100, seed=0, out=DUMMY, nacc=DUMMY, ws=DUMMY, ws_bytes=1 << 30, dbg=None, stream=None)
+    a.update(kw)
+    return lib.rs_verify_filtered(a["logits"], a["dtype"], a["q"], a["draft"], a["cu"], a["T"], a["top_k"],
+                                  a["top_p"], a["B"], a["D"], a["max_k"], a["V"], a["seed"], a["out"], a["nacc"],
+                                  a["ws"], a["ws_bytes"], a["dbg"], a["stream"])
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(V=1 << 20), rs.RS_ERR_UNSUPPORTED),            # fixed-point top-p masses need V < 2^20
+    (dict(V=1 << 20, top_k=None), rs.RS_ERR_UNSUPPORTED),
+    (dict(top_k=DUMMY + 2), rs.RS_ERR_UNSUPPORTED),      # int32 alignment
+    (dict(top_p=DUMMY + 1), rs.RS_ERR_UNSUPPORTED),
+    (dict(max_k=33, D=4), rs.RS_ERR_INVALID_ARG),
+    (dict(T=None), rs.RS_ERR_INVALID_ARG),
+    (dict(ws_bytes=16), rs.RS_ERR_WORKSPACE),
+])
+def test_filtered_entry_validation(lib, kw, status):
+    assert _call_filtered(lib, **kw) == status
+
+
+@needs_no_gpu
+def test_filtered_entry_empty_batch(lib):
+    assert _call_filtered(lib, B=0, D=0, logits=None, out=None, nacc=None, ws=None) == rs.RS_OK

@@ -138,6 +138,12 @@ typedef struct rs_debug {
 size_t rs_verify_workspace_size(int32_t batch, int32_t total_draft_tokens, int32_t max_k,
                                 int32_t vocab, rs_dtype logits_dtype);
 
+/* Bytes of workspace rs_verify_filtered needs with top_k or top_p given: the
+ * rs_verify workspace plus one fp32 maximum per 4096-byte segment of every
+ * logits row (5 KB per row at V = 151936 bf16).  Returns 0 for invalid sizes. */
+size_t rs_verify_filtered_workspace_size(int32_t batch, int32_t total_draft_tokens, int32_t max_k,
+                                         int32_t vocab, rs_dtype logits_dtype);
+
 /* Batched verify (random and greedy requests mixed; T <= 0 is greedy).
  *   target_logits       [R, V] fp32 or bf16, element-aligned
  *   draft_probs         [D, V] fp32 or NULL (one-hot q at the draft)
@@ -174,11 +180,14 @@ rs_status rs_verify(const void* target_logits, rs_dtype logits_dtype, const floa
  *   top_k        [B] int32 device, or NULL; top_k[b] <= 0 or >= V: no top-k
  *   top_p        [B] fp32 device, or NULL; top_p[b] outside (0, 1): no top-p
  * Greedy requests (T <= 0) ignore both.  Every other argument, the layout,
- * ownership, workspace size (rs_verify_workspace_size) and error rules are
- * those of rs_verify; additionally V must be below 2^20 when top_k or top_p
- * is given (RS_ERR_UNSUPPORTED otherwise).  Filtered calls run the phased
- * path: one 1024-thread workgroup per needed row finds the row's threshold
- * by radix selection before the accept tests. */
+ * ownership and error rules are those of rs_verify, except that the workspace
+ * must hold rs_verify_filtered_workspace_size bytes when top_k or top_p is
+ * given (RS_ERR_WORKSPACE otherwise), and that V must then be below 2^20
+ * (RS_ERR_UNSUPPORTED otherwise).  Filtered calls run the phased path: the
+ * row statistics pass also records per-segment maxima of filtered rows, and a
+ * small kernel per phase finds each such row's threshold by radix selection
+ * over the few segments that can hold kept tokens before the accept tests.
+ * With top_k and top_p both NULL this is exactly rs_verify. */
 rs_status rs_verify_filtered(const void* target_logits, rs_dtype logits_dtype, const float* draft_probs,
                              const int32_t* draft_token_ids, const int32_t* cu_num_draft_tokens,
                              const float* temperature, const int32_t* top_k, const float* top_p,

@@ -63,6 +63,8 @@ def load_library(path: str = LIB_PATH):
     P, i32, u64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
     lib.rs_verify_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.c_int]
     lib.rs_verify_workspace_size.restype = sz
+    lib.rs_verify_filtered_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.c_int]
+    lib.rs_verify_filtered_workspace_size.restype = sz
     lib.rs_verify.argtypes = [P, ctypes.c_int, P, P, P, P, i32, i32, i32, i32, u64, P, P, P, sz, P, P]
     lib.rs_verify.restype = ctypes.c_int
     lib.rs_verify_filtered.argtypes = [P, ctypes.c_int, P, P, P, P, P, P, i32, i32, i32, i32, u64, P, P, P, sz, P,
@@ -85,10 +87,14 @@ def _check(status: int):
 
 
 def workspace_size(batch: int, total_draft_tokens: int, max_k: int, vocab: int,
-                   dtype: torch.dtype = torch.bfloat16) -> int:
+                   dtype: torch.dtype = torch.bfloat16, filtered: bool = False) -> int:
+    """Workspace bytes for rs_verify / rs_verify_greedy, or for rs_verify_filtered
+    with top-k / top-p (filtered=True)."""
     if dtype not in _DTYPE:
         raise ValueError(f"unsupported logits dtype {dtype}")
-    return int(load_library().rs_verify_workspace_size(batch, total_draft_tokens, max_k, vocab, _DTYPE[dtype]))
+    lib = load_library()
+    f = lib.rs_verify_filtered_workspace_size if filtered else lib.rs_verify_workspace_size
+    return int(f(batch, total_draft_tokens, max_k, vocab, _DTYPE[dtype]))
 
 
 @dataclass
@@ -143,7 +149,7 @@ def _dev_tensor(t: torch.Tensor, name: str, dtype, device) -> torch.Tensor:
 
 
 def _common(target_logits, draft_token_ids, cu_num_draft_tokens, max_k, out, num_accepted, workspace,
-            stream):
+            stream, filtered=False):
     if not isinstance(target_logits, torch.Tensor) or target_logits.device.type != "cuda":
         raise ValueError("target_logits must be a CUDA (HIP) tensor")
     dev = target_logits.device
@@ -172,7 +178,7 @@ def _common(target_logits, draft_token_ids, cu_num_draft_tokens, max_k, out, num
     if out.numel() != B * (max_k + 1) or num_accepted.numel() != B:
         raise ValueError("out must hold B * (max_k + 1) and num_accepted B int32 values")
     if workspace is None:
-        n = workspace_size(B, D, max_k, V, target_logits.dtype) if B > 0 else 0
+        n = workspace_size(B, D, max_k, V, target_logits.dtype, filtered) if B > 0 else 0
         workspace = torch.empty((max(n, 1),), dtype=torch.uint8, device=dev)
     _dev_tensor(workspace, "workspace", torch.uint8, dev)
     if stream is None:
@@ -193,7 +199,8 @@ def verify(target_logits: torch.Tensor, draft_probs: Optional[torch.Tensor], dra
     rs_verify."""
     lib = load_library()
     dev, B, D, V, out, num_accepted, workspace, stream = _common(
-        target_logits, draft_token_ids, cu_num_draft_tokens, max_k, out, num_accepted, workspace, stream)
+        target_logits, draft_token_ids, cu_num_draft_tokens, max_k, out, num_accepted, workspace, stream,
+        filtered=top_k is not None or top_p is not None)
     _dev_tensor(temperature, "temperature", torch.float32, dev)
     if temperature.numel() != B:
         raise ValueError("temperature must have B entries")

@@ -1,4 +1,4 @@
-// Top-k / top-p filtering of the target distribution, one workgroup per row.
+// Top-k / top-p filtering of the target distribution.
 //
 // Rejection sampling constrains the target distribution with the temperature,
 // top-k and top-p before the accept test, the residual and the bonus
@@ -10,16 +10,28 @@
 // so the kept set is {x : l_x >= tau} for one threshold logit tau per row, and
 // p' = exp2(l c - shift) / S' on it, S' the kept mass.
 //
-// The kernel finds tau exactly by radix selection on order-preserving 32-bit
-// keys of the logits (bf16 logits only use the upper 16 bits): a 4096-bin
-// histogram of the top 12 key bits, then of the next 12 (then of the last 8
-// for fp32), each time narrowing to the bin where the cumulative count (top-k)
-// or mass (top-p) from the top reaches the target.  Histograms live in LDS;
-// masses are fixed point (exp2 value scaled by 2^44, truncated, u64), so the
-// selection is deterministic.  The row stays in registers between passes when
-// it fits (1024 threads x kFilterResident 16-byte vectors), otherwise later
-// passes re-read it.  The workgroup also gathers l(x*) and q(x*) for the
-// accept test, so the row statistics pass skips filtered rows entirely.
+// A filtered row is first streamed by the ordinary row-statistics task, which
+// also stores every thread's maximum of its 16 x 16-byte "segment" of the row
+// (chunk_task's tmax).  filter_kernel then works per row from those maxima:
+//   * the k-th largest segment maximum bounds the k-th largest logit from
+//     below (k segments hold an element at least that large); the segment
+//     maxima, taken from the top until their mass reaches the top-p target,
+//     likewise bound the top-p threshold;
+//   * only the segments whose maximum reaches the bound can hold a kept
+//     token: they are re-read (a few KB per row) and their elements at or
+//     above the bound copied to an LDS list;
+//   * tau is found exactly on that list: by ranking (each value against all
+//     others) for lists of up to 256 values, else by radix selection on
+//     order-preserving 32-bit keys of the logits (bf16 logits use the upper
+//     16 bits) with 8-bit digits -- a 256-bin LDS histogram per digit, each
+//     time narrowing to the bin where the cumulative count (top-k) or mass
+//     (top-p) from the top reaches the target.  Masses are fixed point (exp2
+//     value scaled by 2^44, truncated, u64), so the selection is
+//     deterministic;
+//   * S' is summed over the list.
+// When no bound can be formed (k above the number of segments, segment maxima
+// lighter than the top-p target) or the list overflows, the selection runs
+// over the whole row, re-read from memory (select_row).
 #pragma once
 
 #include "common.hpp"
@@ -27,10 +39,17 @@
 
 namespace rsv {
 
-constexpr int kFilterThreads = 1024;
-constexpr int kFilterBinBits = 12;
-constexpr int kFilterBins = 1 << kFilterBinBits;  // 4 per thread
-constexpr int kFilterResident = 16;               // 16-byte vectors per thread kept in registers
+constexpr int kFilterThreads = 256;
+constexpr int kFilterBins = 256;      // one radix digit of 8 bits: one bin per thread
+// Histogram copies, chosen by lane & 3, so fewer lanes of one wavefront
+// instruction add to the same LDS word (same-address atomics serialise); copy
+// c starts at c * kHistStride words so equal bins of different copies sit in
+// different banks.
+constexpr int kHistCopies = 4;
+constexpr int kHistStride = kFilterBins + 1;
+constexpr int kFilterCand = 4096;     // candidate list entries in LDS
+constexpr int kFilterSegList = 1024;  // segments re-read per row at most
+constexpr int kSegVectors = 16;       // 16-byte vectors per segment: the row task's vectors per thread
 
 // Per-row result: keep l >= tau; shift = fl32(max * c); sum = S' (fp64).
 struct FilterRec {
@@ -63,38 +82,8 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// The elements of one row as seen by one thread: resident vectors, vectors
-// beyond them (re-read), and at most one unaligned head / tail element.
-template <typename Elem>
-struct FilterRow {
-  const uint4* pv;
-  int nvec;
-  float extra;  // -inf when the thread has none (harmless for every pass below)
-  bool has_extra;
-  uint4 res[kFilterResident];
-
-  template <typename F>
-  __device__ __forceinline__ void visit(F&& f) const {
-    using VT = Vec<Elem>;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < kFilterResident; ++i) {
-      if (tid + i * kFilterThreads < nvec) {
-#pragma unroll
-        for (int k = 0; k < VT::W; ++k) f(VT::get(res[i], k));
-      }
-    }
-    for (int v = tid + kFilterResident * kFilterThreads; v < nvec; v += kFilterThreads) {
-      const uint4 x = pv[v];
-#pragma unroll
-      for (int k = 0; k < VT::W; ++k) f(VT::get(x, k));
-    }
-    if (has_extra) f(extra);
-  }
-};
-
 // Fixed-point mass of one element: floor(e * 2^44), e = exp2(l c - shift) in
-// [0, 1 + 2^-23]; a row of V < 2^19 such values sums below 2^63.
+// [0, 1 + 2^-23]; a row of V < 2^20 such values sums below 2^64.
 __device__ __forceinline__ unsigned long long fixed_mass(float e) {
   const float x = e * 0x1p+12f;  // integer part < 2^12 + 1, fraction on a 2^-32 grid or finer (truncated)
   const uint32_t hi = (uint32_t)x;
@@ -102,22 +91,108 @@ __device__ __forceinline__ unsigned long long fixed_mass(float e) {
   return ((unsigned long long)hi << 32) | lo;
 }
 
-// Find the bin B of hist[] (kFilterBins u64 weights) where, counting from the
-// top bin down, base + (weight of the bins above B) < target <= base + (weight
-// of the bins from B up).  Returns B and adds the weight above B to *base;
-// -1 if the target exceeds the total.  Whole workgroup; thread t owns bins
-// 4t .. 4t+3.  s_u64 needs kFilterThreads / 64 + 2 slots.
+// One row split into an unaligned head, 16-byte vectors and a tail, exactly as
+// the row-statistics task splits it.
+template <typename Elem>
+struct RowView {
+  const Elem* prow;
+  const uint4* pv;
+  int head, nvec, tail;
+  __device__ __forceinline__ RowView(const Elem* p, int32_t V) : prow(p) {
+    constexpr int W = Vec<Elem>::W;
+    head = (int)(((16u - ((uint32_t)(uintptr_t)p & 15u)) & 15u) / sizeof(Elem));
+    if (head > V) head = V;
+    nvec = (V - head) / W;
+    tail = V - head - nvec * W;
+    pv = reinterpret_cast<const uint4*>(p + head);
+  }
+  // The head / tail element held by thread t of chunk 0 in the row task (a
+  // row task thread t < head holds prow[t]; 8 <= t < 8 + tail a tail element).
+  __device__ __forceinline__ bool extra(int t, float& v) const {
+    constexpr int W = Vec<Elem>::W;
+    if (t < head) {
+      v = to_f32(prow[t]);
+      return true;
+    }
+    if (t >= 8 && t - 8 < tail) {
+      v = to_f32(prow[head + nvec * W + (t - 8)]);
+      return true;
+    }
+    return false;
+  }
+};
+
+// Element visitors for the selection: each calls f(value) for the elements
+// the calling thread holds.
+template <typename Elem>
+struct RowVisitor {  // the whole row, read from memory kRowBatch vectors per thread at a time
+  static constexpr int kRowBatch = 16;
+  RowView<Elem> rv;
+  template <typename F>
+  __device__ __forceinline__ void operator()(F&& f) const {
+    using VT = Vec<Elem>;
+    for (int v0 = threadIdx.x; v0 < rv.nvec; v0 += kRowBatch * kFilterThreads) {
+      // unconditional loads (clamped index), so all kRowBatch are in flight together
+      uint4 x[kRowBatch];
+#pragma unroll
+      for (int i = 0; i < kRowBatch; ++i) x[i] = rv.pv[min(v0 + i * kFilterThreads, rv.nvec - 1)];
+#pragma unroll
+      for (int i = 0; i < kRowBatch; ++i) {
+        if (v0 + i * kFilterThreads < rv.nvec) {
+#pragma unroll
+          for (int k = 0; k < VT::W; ++k) f(VT::get(x[i], k));
+        }
+      }
+    }
+    float e;
+    if (threadIdx.x < 16 && rv.extra(threadIdx.x, e)) f(e);
+  }
+};
+constexpr int kSegPerThread = 16;  // segment maxima a thread keeps in registers (rows of up to 4096 segments)
+
+struct MaxVisitor {  // the segment maxima, kSegPerThread per thread in registers
+  const float (&mx)[kSegPerThread];
+  template <typename F>
+  __device__ __forceinline__ void operator()(F&& f) const {
+#pragma unroll
+    for (int i = 0; i < kSegPerThread; ++i)
+      if (mx[i] > -INFINITY) f(mx[i]);
+  }
+};
+struct ListVisitor {  // a candidate list in LDS
+  const float* vals;
+  int n;
+  template <typename F>
+  __device__ __forceinline__ void operator()(F&& f) const {
+    for (int i = threadIdx.x; i < n; i += kFilterThreads) {
+      const float v = vals[i];
+      if (v > -INFINITY) f(v);
+    }
+  }
+};
+
+__device__ __forceinline__ void hist_clear(unsigned long long* hist) {
+#pragma unroll
+  for (int c = 0; c < kHistCopies; ++c) hist[c * kHistStride + threadIdx.x] = 0ull;
+}
+__device__ __forceinline__ void hist_add(unsigned long long* hist, int bin, unsigned long long w) {
+  atomicAdd(hist + (threadIdx.x & (kHistCopies - 1)) * kHistStride + bin, w);
+}
+
+// Find the bin B of hist[] (kFilterBins = kFilterThreads u64 weights, thread
+// t owning bin t) where, counting from the top bin down, base + (weight of
+// the bins above B) < target <= base + (weight of the bins from B up).
+// Returns B and adds the weight above B to base; -1 if the target exceeds the
+// total.  Whole workgroup.  s_u64 needs kFilterThreads / 64 + 1 slots.
 __device__ __forceinline__ int find_bin(const unsigned long long* hist, double target, unsigned long long& base,
                                         unsigned long long* s_u64, int* s_bin) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int NW = kFilterThreads / 64;
-  __syncthreads();  // earlier readers of s_u64 / s_bin are done
-  unsigned long long h[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __syncthreads();  // the histogram is complete; earlier readers of s_u64 / s_bin are done
+  unsigned long long h = 0ull;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) h[i] = hist[4 * tid + i];
-  const unsigned long long tot = h[0] + h[1] + h[2] + h[3];
-  // suffix sums over the lanes of the wave, then over the waves
-  unsigned long long suf = tot;
+  for (int c = 0; c < kHistCopies; ++c) h += hist[c * kHistStride + tid];
+  unsigned long long suf = h;  // suffix sums over the lanes of the wave, then over the waves
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const unsigned long long v = __shfl_down(suf, o);
@@ -126,85 +201,266 @@ __device__ __forceinline__ int find_bin(const unsigned long long* hist, double t
   if (tid == 0) *s_bin = -1;
   if (lane == 0) s_u64[wave] = suf;
   __syncthreads();
-  unsigned long long above = base + (suf - tot);
+  unsigned long long above = base + (suf - h);
   for (int w = wave + 1; w < NW; ++w) above += s_u64[w];
-#pragma unroll
-  for (int i = 3; i >= 0; --i) {
-    if ((double)above < target && (double)(above + h[i]) >= target) {
-      *s_bin = 4 * tid + i;
-      s_u64[NW] = above;
-    }
-    above += h[i];
+  if ((double)above < target && (double)(above + h) >= target) {
+    *s_bin = tid;
+    s_u64[NW] = above;
   }
   __syncthreads();
   const int bin = *s_bin;
   if (bin >= 0) base = s_u64[NW];
-  __syncthreads();  // s_u64 and s_bin are reused
+  __syncthreads();  // s_u64, s_bin and hist are reused
   return bin;
 }
 
-// Total of hist[] (whole workgroup).
-__device__ __forceinline__ unsigned long long hist_total(const unsigned long long* hist, unsigned long long* s_u64) {
-  const int tid = threadIdx.x;
-  unsigned long long t = hist[4 * tid] + hist[4 * tid + 1] + hist[4 * tid + 2] + hist[4 * tid + 3];
-  return block_reduce<kFilterThreads>(t, s_u64, SumOp());
-}
-
-// Radix selection: the key kappa such that, over the elements with key >=
-// kmin, weight(key > kappa) < target <= weight(key >= kappa), weights being 1
-// (MASS = false) or the fixed-point mass.  With MASS and top_p > 0 the target
-// is top_p times the total weight (taken from the first histogram).
-template <typename Elem, bool MASS>
-__device__ __forceinline__ uint32_t radix_select(const FilterRow<Elem>& row, uint32_t kmin, double target,
-                                                 float top_p, float cs, float shift, unsigned long long* hist,
-                                                 unsigned long long* s_u64, int* s_bin) {
-  const int tid = threadIdx.x;
-  constexpr int levels = sizeof(Elem) == 2 ? 2 : 3;  // bf16 keys end in 16 constant bits
+// Radix selection with 8-bit digits: the key kappa such that, over the
+// visited elements with key >= kmin, weight(key > kappa) < target <=
+// weight(key >= kappa), weights being 1 (MASS = false) or the fixed-point
+// mass.  With fewer than all levels (nlev) it returns the smallest key of the
+// group that holds kappa -- a lower bound of it.  Returns 0 (no float has key
+// 0) when the target exceeds the total weight.
+template <typename Elem, bool MASS, typename Vis>
+__device__ __forceinline__ uint32_t radix_select(const Vis& vis, uint32_t kmin, double target, float cs, float shift,
+                                                 int nlev, unsigned long long* hist, unsigned long long* s_u64,
+                                                 int* s_bin) {
+  constexpr int kLevels = sizeof(Elem) == 2 ? 2 : 4;  // bf16 keys end in 16 constant bits
   uint32_t prefix = 0, pmask = 0;
   unsigned long long base = 0;
-#pragma unroll
-  for (int lv = 0; lv < levels; ++lv) {
-    const int sh = lv == 0 ? 20 : (lv == 1 ? 8 : 0);
-    const uint32_t bmask = lv == 2 ? 0xFFu : (uint32_t)(kFilterBins - 1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hist[4 * tid + i] = 0ull;
+  for (int lv = 0; lv < kLevels && lv < nlev; ++lv) {
+    const int sh = 24 - 8 * lv;
+    hist_clear(hist);
     __syncthreads();
-    row.visit([&](float l) {
+    vis([&](float l) {
       const uint32_t key = order_key(l);
       if (key >= kmin && (key & pmask) == prefix) {
         const unsigned long long w = MASS ? fixed_mass(exp2_hw(fmaf(l, cs, -shift))) : 1ull;
-        if (w) atomicAdd(hist + ((key >> sh) & bmask), w);
+        if (w) hist_add(hist, (int)((key >> sh) & 0xFFu), w);
+      }
+    });
+    const int bin = find_bin(hist, target, base, s_u64, s_bin);
+    if (bin < 0) return 0u;
+    prefix |= (uint32_t)bin << sh;
+    pmask |= 0xFFu << sh;
+  }
+  return prefix;  // bf16: the low 16 bits stay 0, below every key of the selected value and above the next
+}
+
+// The same selection over a list of at most kFilterThreads values in LDS, one
+// per thread, by ranking: value v_i is the answer iff the weight of the
+// values > v_i is below the target and the weight of those >= v_i reaches it.
+template <bool MASS>
+__device__ __forceinline__ uint32_t rank_select(const float* vals, int n, uint32_t kmin, double target, float cs,
+                                                float shift, unsigned long long* wts, uint32_t* s_key) {
+  const int tid = threadIdx.x;
+  __syncthreads();
+  float v = -INFINITY;
+  uint32_t kv = 0u;
+  if (tid < n) {
+    v = vals[tid];
+    kv = order_key(v);
+    wts[tid] = (kv >= kmin) ? (MASS ? fixed_mass(exp2_hw(fmaf(v, cs, -shift))) : 1ull) : 0ull;
+  }
+  if (tid == 0) *s_key = 0u;
+  __syncthreads();
+  if (tid < n && kv >= kmin) {
+    unsigned long long gt = 0ull, eq = 0ull;
+    for (int i = 0; i < n; ++i) {
+      const float u = vals[i];
+      const unsigned long long w = wts[i];
+      gt += u > v ? w : 0ull;
+      eq += u == v ? w : 0ull;
+    }
+    if ((double)gt < target && (double)(gt + eq) >= target) *s_key = kv;  // equal values write the same key
+  }
+  __syncthreads();
+  const uint32_t k = *s_key;
+  __syncthreads();
+  return k;
+}
+
+// Sum over the visited elements with key >= kmin of the fixed-point mass
+// (whole workgroup).
+template <typename Vis>
+__device__ __forceinline__ unsigned long long fixed_total(const Vis& vis, uint32_t kmin, float cs, float shift,
+                                                          unsigned long long* s_u64) {
+  unsigned long long t = 0ull;
+  vis([&](float l) {
+    if (order_key(l) >= kmin) t += fixed_mass(exp2_hw(fmaf(l, cs, -shift)));
+  });
+  return block_reduce<kFilterThreads>(t, s_u64, SumOp());
+}
+
+// Copy into cand[] every element >= t of the segments whose maximum is >= t
+// (segment sg = threadIdx.x + i * kFilterThreads has maximum mx[i]: row-task
+// chunk sg / 256, thread sg % 256, holding vectors chunk * 4096 + thread +
+// u * 256 for u < 16, plus a head / tail element in chunk 0).  The segments
+// are listed first, then all threads share their (segment, vector) loads.
+// Returns the element count, or -1 if the segments or the elements overflow
+// their lists.
+template <typename Elem>
+__device__ __forceinline__ int gather_segments(const RowView<Elem>& rv, const float (&mx)[kSegPerThread], float t,
+                                               float* cand, int* qseg, int* s_cnt, int* s_nq) {
+  using VT = Vec<Elem>;
+  constexpr int kItems = kSegVectors + 1;  // 16 vectors and the head / tail element
+  constexpr int kBatch = 4;
+  const int tid = threadIdx.x;
+  __syncthreads();
+  if (tid == 0) {
+    *s_cnt = 0;
+    *s_nq = 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kSegPerThread; ++i) {
+    if (mx[i] >= t) {
+      const int slot = atomicAdd(s_nq, 1);
+      if (slot < kFilterSegList) qseg[slot] = tid + i * kFilterThreads;
+    }
+  }
+  __syncthreads();
+  const int nq = *s_nq;
+  if (nq > kFilterSegList || rv.nvec == 0) return -1;  // (rows shorter than one vector: whole-row selection)
+  auto put = [&](float l) {
+    if (l >= t) {
+      const int slot = atomicAdd(s_cnt, 1);
+      if (slot < kFilterCand) cand[slot] = l;
+    }
+  };
+  const int nitems = nq * kItems;
+  for (int it0 = tid; it0 < nitems; it0 += kBatch * kFilterThreads) {
+    uint4 x[kBatch];
+    float ex[kBatch];
+    int kind[kBatch];  // 0 none, 1 vector, 2 extra element
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) {  // vector loads unconditional (clamped index): all in flight together
+      const int it = it0 + r * kFilterThreads;
+      const int sg = qseg[min(it, nitems - 1) / kItems], u = it % kItems;
+      const int c = sg / kRowThreads, th = sg % kRowThreads;
+      const int v = c * kSegVectors * kRowThreads + th + u * kRowThreads;
+      x[r] = rv.pv[min(v, rv.nvec - 1)];
+      kind[r] = 0;
+      if (it < nitems) {
+        if (u < kSegVectors) {
+          if (v < rv.nvec) kind[r] = 1;
+        } else if (c == 0 && rv.extra(th, ex[r])) {
+          kind[r] = 2;
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) {
+      if (kind[r] == 1) {
+#pragma unroll
+        for (int k = 0; k < VT::W; ++k) put(VT::get(x[r], k));
+      } else if (kind[r] == 2) {
+        put(ex[r]);
+      }
+    }
+  }
+  __syncthreads();
+  const int n = *s_cnt;
+  return n <= kFilterCand ? n : -1;
+}
+
+// Selection over the whole row (no usable bound).  Elements are binned by
+// their distance below the row maximum in log2(e) units, d = shift - l c:
+// first only those within 16 bits of the maximum, 16 bins per bit (the
+// others are skipped at the cost of a compare, and in practice the threshold
+// lies there); if that window holds less than the target weight, then the
+// whole row with 4 bins per bit and everything beyond 64 bits in the lowest
+// bin.  Larger logits go to higher bins.  The bin where the cumulative weight
+// from the top reaches the target is gathered and selected exactly, with the
+// target less the weight above it.  If that bin overflows the candidate list,
+// radix selection runs on the keys of the whole row.  The candidate list is
+// left holding only that bin.
+//
+// On return n_out is the number of candidates (the elements of the selected
+// bin) and base_out the weight above that bin, or n_out = -1 when the radix
+// selection over the row's keys ran instead.
+template <typename Elem, bool MASS>
+__device__ __forceinline__ uint32_t select_row(const RowVisitor<Elem>& all, uint32_t kmin, double target, float cs,
+                                               float shift, float* cand, unsigned long long* hist,
+                                               unsigned long long* wts, unsigned long long* s_u64, int* s_bin,
+                                               uint32_t* s_key, int* s_cnt, int& n_out,
+                                               unsigned long long& base_out) {
+  n_out = -1;
+#pragma unroll 1
+  for (int wide = 0; wide < 2; ++wide) {
+    const float per_bit = wide ? 4.f : 16.f;
+    auto dbin = [&](float l) -> int {  // -1: outside the window
+      const float d = -fmaf(l, cs, -shift) * per_bit;  // >= about 0; +inf for l = -inf
+      if (!wide && !(d < 256.f)) return -1;
+      return 255 - (int)fminf(fmaxf(d, 0.f), 255.f);
+    };
+    // Cheap pre-tests on the logit itself (one compare per element) with a
+    // margin of 1/16 bit; the exact bin test follows for the few that pass.
+    const float lo_win = wide ? -INFINITY : (shift - 16.0625f) / cs;
+    hist_clear(hist);
+    auto process = [&](float l) {
+      const int bin = dbin(l);
+      if (bin >= 0 && order_key(l) >= kmin) {
+        const unsigned long long w = MASS ? fixed_mass(exp2_hw(fmaf(l, cs, -shift))) : 1ull;
+        if (w) hist_add(hist, bin, w);
+      }
+    };
+    __syncthreads();
+    all([&](float l) {
+      if (l >= lo_win) process(l);
+    });
+    unsigned long long base = 0ull;
+    const int B = find_bin(hist, target, base, s_u64, s_bin);
+    if (B < 0) continue;  // the window holds less than the target
+    // logits of bin B lie in ((shift - d_hi) / c, (shift - d_lo) / c]; pre-test with a margin
+    const float d_lo = (float)(255 - B) / per_bit - 0.0625f, d_hi = (float)(256 - B) / per_bit + 0.0625f;
+    const float lo_b = (B == 0 && wide) ? -INFINITY : (shift - d_hi) / cs, hi_b = (shift - d_lo) / cs;
+    if (threadIdx.x == 0) *s_cnt = 0;
+    __syncthreads();
+    all([&](float l) {
+      if (l >= lo_b && l <= hi_b && dbin(l) == B && order_key(l) >= kmin) {
+        const int slot = atomicAdd(s_cnt, 1);
+        if (slot < kFilterCand) cand[slot] = l;
       }
     });
     __syncthreads();
-    if (MASS && lv == 0) target = (double)top_p * (double)hist_total(hist, s_u64);
-    const int bin = find_bin(hist, target, base, s_u64, s_bin);
-    if (bin < 0) return kmin;  // cannot happen for a target within the total; keep everything
-    prefix |= (uint32_t)bin << sh;
-    pmask |= bmask << sh;
+    const int n = *s_cnt;
+    const double rest = target - (double)base;
+    if (n > kFilterCand) return radix_select<Elem, MASS>(all, kmin, target, cs, shift, 4, hist, s_u64, s_bin);
+    n_out = n;
+    base_out = base;
+    if (n <= kFilterThreads) return rank_select<MASS>(cand, n, kmin, rest, cs, shift, wts, s_key);
+    return radix_select<Elem, MASS>(ListVisitor{cand, n}, kmin, rest, cs, shift, 4, hist, s_u64, s_bin);
   }
-  if (levels == 2) prefix |= (prefix & 0x80000000u) ? 0u : 0xFFu;  // bf16: low bits follow the sign
-  return prefix;
+  return 0u;
+}
+
+// Select over the candidate list: ranking for short lists, radix otherwise.
+template <typename Elem, bool MASS>
+__device__ __forceinline__ uint32_t select_list(const float* cand, int n, uint32_t kmin, double target, float cs,
+                                                float shift, unsigned long long* hist, unsigned long long* wts,
+                                                unsigned long long* s_u64, int* s_bin, uint32_t* s_key) {
+  if (n <= kFilterThreads) return rank_select<MASS>(cand, n, kmin, target, cs, shift, wts, s_key);
+  return radix_select<Elem, MASS>(ListVisitor{cand, n}, kmin, target, cs, shift, 4, hist, s_u64, s_bin);
 }
 
 // One workgroup per (request, position) row of the positions [j_begin,
 // j_begin + j_count) of every random request with a filter (and, after the
-// first phase, still active): writes frec[row] and, for a draft position, the
-// gathers l(x*), q(x*).
+// first phase, still active), after the row task streamed it: writes
+// frec[row] from the row's partials and segment maxima.
 template <typename Elem>
 __global__ __launch_bounds__(kFilterThreads) void filter_kernel(
-    const Elem* __restrict__ logits, const float* __restrict__ q, const int32_t* __restrict__ draft,
-    const int32_t* __restrict__ cu, const float* __restrict__ temperature, const int32_t* __restrict__ top_k,
-    const float* __restrict__ top_p, int32_t D, int32_t max_k, int32_t V, int32_t j_begin, int32_t j_count,
-    const ReqRecord* __restrict__ records, FilterRec* __restrict__ frec, Gathered* __restrict__ gath) {
-  using VT = Vec<Elem>;
-  constexpr int W = VT::W;
-  __shared__ unsigned long long hist[kFilterBins];
-  __shared__ unsigned long long s_u64[kFilterThreads / 64 + 2];
-  __shared__ float s_f[kFilterThreads / 64];
+    const Elem* __restrict__ logits, const int32_t* __restrict__ cu, const float* __restrict__ temperature,
+    const int32_t* __restrict__ top_k, const float* __restrict__ top_p, int32_t D, int32_t max_k, int32_t V,
+    int32_t j_begin, int32_t j_count, int32_t nsplit, const ReqRecord* __restrict__ records,
+    const RowPartial* __restrict__ partials, const float* __restrict__ tmaxbuf, FilterRec* __restrict__ frec) {
+  __shared__ unsigned long long hist[kHistCopies * kHistStride];
+  __shared__ unsigned long long wts[kFilterThreads];
+  __shared__ float cand[kFilterCand];
+  __shared__ int qseg[kFilterSegList];
+  __shared__ unsigned long long s_u64[kFilterThreads / 64 + 1];
   __shared__ double s_d[kFilterThreads / 64];
-  __shared__ int s_bin;
-  const int tid = threadIdx.x;
+  __shared__ int s_bin, s_cnt, s_nq;
+  __shared__ uint32_t s_key;
   const int32_t j = j_begin + (int32_t)(blockIdx.x % j_count);
   const int32_t b = (int32_t)(blockIdx.x / j_count);
   const int32_t s = cu[b], e = cu[b + 1];
@@ -212,62 +468,93 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(
   const float T = temperature[b];
   if (!(T > 0.f) || !filter_on(top_k, top_p, b, V)) return;
   if (j_begin > 0 && records[b].mode != kModeActive) return;
-  const int32_t K = e - s;
   const float cs = scale_of(T);
   const int64_t row = (int64_t)s + b + j;
-  const Elem* prow = logits + row * (int64_t)V;
+  const RowView<Elem> rv(logits + row * (int64_t)V, V);
+  const RowVisitor<Elem> all{rv};
+  const int nseg = nsplit * kRowThreads;
+  const float* tmax = tmaxbuf + row * nseg;
+  // the row's segment maxima, kSegPerThread per thread (-inf past the end;
+  // rows with more segments than that select over the whole row)
+  const bool use_maxima = nseg <= kSegPerThread * kFilterThreads;
+  float mx[kSegPerThread];
+#pragma unroll
+  for (int i = 0; i < kSegPerThread; ++i) {  // unconditional loads (clamped index): all in flight together
+    const int sg = threadIdx.x + i * kFilterThreads;
+    const float v = tmax[min(sg, nseg - 1)];
+    mx[i] = (use_maxima && sg < nseg) ? v : -INFINITY;
+  }
+  const MaxVisitor maxima{mx};
+  constexpr int kBoundLevels = 2;  // key bits that bound a threshold from the maxima
 
-  if (j < K && tid == 64) {  // accept-test gathers
-    const int32_t xs = draft[s + j];
-    if (xs >= 0 && xs < V) {
-      Gathered g;
-      g.lstar = to_f32(prow[xs]);
-      g.qstar = q ? q[((int64_t)s + j) * V + xs] : 1.f;
-      gath[s + j] = g;
+  float shift;
+  double S;
+  merge_random(partials + row * nsplit, nsplit, shift, S);
+
+  int nbin = -1;                 // top-p over the row: elements of the threshold's bin in cand[0 .. nbin)
+  unsigned long long above_bin = 0ull;  // and the fixed-point mass above that bin
+  int ncand = -1;       // candidate list: every element >= its bound is in cand[0 .. ncand) (-1: none)
+  uint32_t kappa = 0u;  // keep key >= kappa (0: everything)
+  const int32_t kb = top_k ? top_k[b] : 0;
+  if (kb > 0 && kb < V) {
+    const uint32_t bound =
+        use_maxima
+            ? radix_select<Elem, false>(maxima, 0u, (double)kb, cs, shift, kBoundLevels, hist, s_u64, &s_bin)
+            : 0u;
+    if (bound) ncand = gather_segments(rv, mx, key_value(bound), cand, qseg, &s_cnt, &s_nq);
+    if (ncand >= 0) {
+      kappa = select_list<Elem, false>(cand, ncand, 0u, (double)kb, cs, shift, hist, wts, s_u64, &s_bin, &s_key);
+    } else {
+      int nb;
+      unsigned long long cb;
+      kappa = select_row<Elem, false>(all, 0u, (double)kb, cs, shift, cand, hist, wts, s_u64, &s_bin, &s_key, &s_cnt,
+                                      nb, cb);
     }
   }
-
-  FilterRow<Elem> r;
-  int head = (int)(((16u - ((uint32_t)(uintptr_t)prow & 15u)) & 15u) / sizeof(Elem));
-  if (head > V) head = V;
-  r.nvec = (V - head) / W;
-  const int tail = V - head - r.nvec * W;
-  r.pv = reinterpret_cast<const uint4*>(prow + head);
-#pragma unroll
-  for (int i = 0; i < kFilterResident; ++i) {
-    const int v = tid + i * kFilterThreads;
-    if (v < r.nvec) r.res[i] = r.pv[v];
-  }
-  r.has_extra = false;
-  r.extra = -INFINITY;
-  if (tid < head) {
-    r.extra = to_f32(prow[tid]);
-    r.has_extra = true;
-  } else if (tid >= 8 && tid - 8 < tail) {
-    r.extra = to_f32(prow[head + r.nvec * W + (tid - 8)]);
-    r.has_extra = true;
-  }
-
-  // maximum -> shift, exactly as the row statistics compute it
-  float m = -INFINITY;
-  r.visit([&](float l) { m = fmaxf(m, l); });
-  m = block_reduce<kFilterThreads>(m, s_f, MaxOp());
-  const float shift = m * cs;
-
-  uint32_t kappa = 0u;  // keep key >= kappa
-  const int32_t kb = top_k ? top_k[b] : 0;
-  if (kb > 0 && kb < V) kappa = radix_select<Elem, false>(r, 0u, (double)kb, 0.f, cs, shift, hist, s_u64, &s_bin);
   const float pb = top_p ? top_p[b] : 1.f;
-  if (pb > 0.f && pb < 1.f) kappa = radix_select<Elem, true>(r, kappa, 0.0, pb, cs, shift, hist, s_u64, &s_bin);
+  if (pb > 0.f && pb < 1.f) {
+    // target: top_p times the mass kept by top-k (all of it without top-k)
+    double P;
+    if (kappa == 0u)
+      P = (double)pb * S * 0x1p+44;  // the row's sum in the fixed-point unit
+    else
+      P = (double)pb * (double)(ncand >= 0 ? fixed_total(ListVisitor{cand, ncand}, kappa, cs, shift, s_u64)
+                                           : fixed_total(all, kappa, cs, shift, s_u64));
+    if (ncand < 0) {
+      const uint32_t bound =
+          use_maxima ? radix_select<Elem, true>(maxima, kappa, P, cs, shift, kBoundLevels, hist, s_u64, &s_bin)
+                     : 0u;
+      if (bound) ncand = gather_segments(rv, mx, key_value(bound), cand, qseg, &s_cnt, &s_nq);
+    }
+    uint32_t kp;
+    if (ncand >= 0) {
+      kp = select_list<Elem, true>(cand, ncand, kappa, P, cs, shift, hist, wts, s_u64, &s_bin, &s_key);
+    } else {
+      kp = select_row<Elem, true>(all, kappa, P, cs, shift, cand, hist, wts, s_u64, &s_bin, &s_key, &s_cnt, nbin,
+                                  above_bin);
+    }
+    if (kp) kappa = kp;
+  }
   const float tau = kappa ? key_value(kappa) : -INFINITY;  // key 0 is no float: nothing filtered
 
-  // kept mass S' = sum over l >= tau of exp2(l c - shift), fp64
+  // kept mass S' = sum over l >= tau of exp2(l c - shift): in fp64 over the
+  // candidate list when it holds every kept element (tau >= its bound); from
+  // the fixed-point masses when the selection over the row left the weight
+  // above the threshold's bin and that bin's elements; else over the row
   double acc = 0.0;
-  r.visit([&](float l) {
+  auto add = [&](float l) {
     if (l >= tau) acc += (double)exp2_hw(fmaf(l, cs, -shift));
-  });
-  acc = block_reduce<kFilterThreads>(acc, s_d, SumOp());
-  if (tid == 0) {
+  };
+  if (ncand >= 0) {
+    ListVisitor{cand, ncand}(add);
+    acc = block_reduce<kFilterThreads>(acc, s_d, SumOp());
+  } else if (nbin >= 0 && kappa) {
+    acc = (double)(above_bin + fixed_total(ListVisitor{cand, nbin}, kappa, cs, shift, s_u64)) * 0x1p-44;
+  } else {
+    all(add);
+    acc = block_reduce<kFilterThreads>(acc, s_d, SumOp());
+  }
+  if (threadIdx.x == 0) {
     FilterRec f;
     f.tau = tau;
     f.shift = shift;

@@ -239,11 +239,15 @@ __device__ __forceinline__ RowStats row_stats(const Elem* __restrict__ prow, int
 // Statistics of chunk c (NV vectors per thread) of logits row `row`,
 // written to partials[row * nsplit + c].  Chunk 0 of a draft position's row
 // also stores l(x*) and q(x*) in *gath (x* = xstar, checked by the caller).
+//
+// tmax (NULL: not wanted) receives every thread's own maximum of the chunk
+// (kRowThreads floats, -inf for a thread with no element): the top-k / top-p
+// selection uses them to bound its threshold.
 template <typename Elem, int NV, bool COH = false>
 __device__ __forceinline__ void chunk_task(const Elem* __restrict__ logits, const float* __restrict__ q, int64_t row,
                                            float T, int32_t V, int32_t nsplit, int32_t c, int32_t xstar,
                                            int64_t slot, RowPartial* __restrict__ partials,
-                                           Gathered* __restrict__ gath) {
+                                           Gathered* __restrict__ gath, float* __restrict__ tmax = nullptr) {
   using VT = Vec<Elem>;
   constexpr int W = VT::W;
   __shared__ float lds_f[kRowThreads / 64];
@@ -292,6 +296,7 @@ __device__ __forceinline__ void chunk_task(const Elem* __restrict__ logits, cons
   // Phase 1: chunk maximum.
   float m = full ? chunk_max<Elem, NV, true>(data, v0, tid, nvec, extra)
                  : chunk_max<Elem, NV, false>(data, v0, tid, nvec, extra);
+  if (tmax) tmax[tid] = m;
   m = block_reduce<kRowThreads>(m, lds_f, MaxOp());
 
   RowPartial* out = partials + row * nsplit + c;

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kRowThreads) void phase_kernel(
     int32_t max_k, int32_t V, uint64_t seed, int32_t j_begin, int32_t j_count, int32_t nsplit, int32_t n_row,
     int32_t race_chunks, int32_t n_race, int32_t race_phase, RowPartial* __restrict__ partials,
     Gathered* __restrict__ gath, const ReqRecord* __restrict__ records, unsigned long long* __restrict__ cand,
-    const int32_t* __restrict__ top_k, const float* __restrict__ top_p) {
+    const int32_t* __restrict__ top_k, const float* __restrict__ top_p, float* __restrict__ tmaxbuf) {
   const int32_t id = blockIdx.x;
   const int32_t both = min(n_row, n_race);
   int32_t t;
@@ -79,13 +79,15 @@ __global__ __launch_bounds__(kRowThreads) void phase_kernel(
     if (!request_valid(s, e, D, max_k) || j > e - s) return;
     if (j_begin > 0 && records[b].mode != kModeActive) return;
     const float T = greedy_all ? 0.f : temperature[b];
-    if (T > 0.f && filter_on(top_k, top_p, b, V)) return;  // the filter kernel took this row
     int32_t xstar = -1;
     if (c == 0 && j < e - s && T > 0.f) {
       xstar = draft[s + j];
       if (xstar >= V) xstar = -1;
     }
-    chunk_task<Elem, NV>(logits, q, (int64_t)s + b + j, T, V, nsplit, c, xstar, (int64_t)s + j, partials, gath);
+    const int64_t row = (int64_t)s + b + j;
+    // a filtered row also leaves its segment maxima for the filter kernel
+    float* tmax = (T > 0.f && filter_on(top_k, top_p, b, V)) ? tmaxbuf + (row * nsplit + c) * kRowThreads : nullptr;
+    chunk_task<Elem, NV>(logits, q, row, T, V, nsplit, c, xstar, (int64_t)s + j, partials, gath, tmax);
   } else {
     const int32_t c = t % race_chunks;
     const int32_t b = t / race_chunks;
@@ -196,7 +198,7 @@ struct Plan {
   int bounds[kMaxPhases + 1];
   int stream_lead;      // stream path: positions streamed before races interleave
   size_t off_partials, off_gath, off_records, off_cand;
-  size_t off_row_count, off_masks, off_state, off_race_ctl, off_queue, off_tail, off_frec, total;
+  size_t off_row_count, off_masks, off_state, off_race_ctl, off_queue, off_tail, off_frec, off_tmax, total;
 };
 
 static size_t align_up(size_t v) { return (v + kRegionAlign - 1) / kRegionAlign * kRegionAlign; }
@@ -224,7 +226,9 @@ static bool make_plan(int32_t B, int32_t D, int32_t max_k, int32_t V, rs_dtype d
   p.nvec_max = V / p.W;
   p.nsplit_max = nsplit_for(p.nvec_max, 1);
   const int64_t R = (int64_t)D + B;
-  if (force_nv) {
+  if (filtered) {
+    p.row_nv = kSegVectors;  // the filter kernel reads the row tasks' segments of 16 vectors per thread
+  } else if (force_nv) {
     p.row_nv = force_nv;
   } else {
     p.row_nv = 1;
@@ -287,7 +291,8 @@ static bool make_plan(int32_t B, int32_t D, int32_t max_k, int32_t V, rs_dtype d
   p.off_queue = p.off_race_ctl + align_up((size_t)B * kRaceCtlStride * sizeof(uint32_t));
   p.off_tail = p.off_queue + align_up((size_t)B * sizeof(int32_t));
   p.off_frec = p.off_tail + kRegionAlign;
-  p.total = p.off_frec + align_up((size_t)R * sizeof(FilterRec));
+  p.off_tmax = p.off_frec + align_up((size_t)R * sizeof(FilterRec));
+  p.total = p.off_tmax + (filtered ? align_up((size_t)R * p.nsplit * kRowThreads * sizeof(float)) : 0);
   // 1-D grids must stay below 2^31 workgroups.
   return (int64_t)p.nsplit * L * B + (int64_t)p.race_chunks * B < INT32_MAX;
 }
@@ -324,10 +329,10 @@ static void launch_phase(hipStream_t stream, const Elem* logits, const float* q,
                          const int32_t* cu, const float* temperature, int greedy_all, int32_t D, int32_t max_k,
                          int32_t V, uint64_t seed, const PhaseArgs& a, RowPartial* partials, Gathered* gath,
                          const ReqRecord* records, unsigned long long* cand, const int32_t* top_k,
-                         const float* top_p) {
+                         const float* top_p, float* tmax) {
   phase_kernel<Elem, NV, TPT><<<(unsigned)(a.n_row + a.n_race), kRowThreads, 0, stream>>>(
       logits, q, draft, cu, temperature, greedy_all, D, max_k, V, seed, a.j_begin, a.j_count, a.nsplit, a.n_row,
-      a.race_chunks, a.n_race, a.race_phase, partials, gath, records, cand, top_k, top_p);
+      a.race_chunks, a.n_race, a.race_phase, partials, gath, records, cand, top_k, top_p, tmax);
 }
 
 template <typename Elem>
@@ -335,11 +340,11 @@ static bool dispatch_phase(int nv, int tpt, hipStream_t stream, const Elem* logi
                            const int32_t* draft, const int32_t* cu, const float* temperature, int greedy_all,
                            int32_t D, int32_t max_k, int32_t V, uint64_t seed, const PhaseArgs& a,
                            RowPartial* partials, Gathered* gath, const ReqRecord* records, unsigned long long* cand,
-                           const int32_t* top_k, const float* top_p) {
+                           const int32_t* top_k, const float* top_p, float* tmax) {
 #define RS_PHASE(NV, TPT)                                                                                           \
   if (nv == NV && tpt == TPT) {                                                                                     \
     launch_phase<Elem, NV, TPT>(stream, logits, q, draft, cu, temperature, greedy_all, D, max_k, V, seed, a,        \
-                                partials, gath, records, cand, top_k, top_p);                                       \
+                                partials, gath, records, cand, top_k, top_p, tmax);                                 \
     return true;                                                                                                    \
   }
   RS_PHASE(16, 32)
@@ -390,6 +395,7 @@ static rs_status launch(const void* logits_v, const float* q, const int32_t* dra
   ReqRecord* records = reinterpret_cast<ReqRecord*>(w + p.off_records);
   unsigned long long* cand = reinterpret_cast<unsigned long long*>(w + p.off_cand);
   FilterRec* frec = reinterpret_cast<FilterRec*>(w + p.off_frec);
+  float* tmax = reinterpret_cast<float*>(w + p.off_tmax);
   const bool filtered = !greedy_all && (top_k || top_p);
   double* dbg_p = dbg ? dbg->draft_target_prob : nullptr;
   EventLog evl{dbg};
@@ -451,15 +457,17 @@ static rs_status launch(const void* logits_v, const float* q, const int32_t* dra
       a.race_chunks = p.race_chunks;
       a.n_race = (ph >= 2 && !greedy_all) ? p.race_chunks * B : 0;
       a.race_phase = ph - 1;
-      if (filtered) {  // thresholds and kept mass of the filtered requests' rows of this phase
-        filter_kernel<Elem><<<(unsigned)(a.j_count * B), kFilterThreads, 0, stream>>>(
-            logits, q, draft, cu, temperature, top_k, top_p, D, max_k, V, a.j_begin, a.j_count, records, frec, gath);
-        if (!evl.after_kernel(stream)) return RS_ERR_HIP;
-      }
       if (!dispatch_phase<Elem>(p.row_nv, p.race_tpt, stream, logits, q, draft, cu, temperature, greedy_all, D,
-                                max_k, V, seed, a, partials, gath, records, cand, top_k, top_p))
+                                max_k, V, seed, a, partials, gath, records, cand, top_k, top_p,
+                                filtered ? tmax : nullptr))
         return RS_ERR_INVALID_ARG;
       if (!evl.after_kernel(stream)) return RS_ERR_HIP;
+      if (filtered) {  // thresholds and kept mass of the filtered requests' rows of this phase
+        filter_kernel<Elem><<<(unsigned)(a.j_count * B), kFilterThreads, 0, stream>>>(
+            logits, cu, temperature, top_k, top_p, D, max_k, V, a.j_begin, a.j_count, p.nsplit, records, partials,
+            tmax, frec);
+        if (!evl.after_kernel(stream)) return RS_ERR_HIP;
+      }
       if (dbg && dbg->probs && !greedy_all) {
         probs_kernel<Elem><<<(unsigned)((max_k + 1) * B), 256, 0, stream>>>(
             logits, cu, temperature, D, max_k, V, p.nsplit, partials, dbg->probs, top_k, top_p, frec);
@@ -481,7 +489,7 @@ static rs_status launch(const void* logits_v, const float* q, const int32_t* dra
       a.n_race = p.race_chunks * B;
       a.race_phase = p.nphases;
       if (!dispatch_phase<Elem>(p.row_nv, p.race_tpt, stream, logits, q, draft, cu, temperature, greedy_all, D,
-                                max_k, V, seed, a, partials, gath, records, cand, top_k, top_p))
+                                max_k, V, seed, a, partials, gath, records, cand, top_k, top_p, nullptr))
         return RS_ERR_INVALID_ARG;
       if (!evl.after_kernel(stream)) return RS_ERR_HIP;
       emit_kernel<Elem><<<(unsigned)B, 64, 0, stream>>>(logits, draft, max_k, V, p.race_chunks, seed, records, cand,
@@ -535,14 +543,24 @@ static rs_status verify_impl(const void* logits, rs_dtype dt, const float* q, co
 
 extern "C" {
 
-size_t rs_verify_workspace_size(int32_t batch, int32_t total_draft_tokens, int32_t max_k, int32_t vocab,
-                                rs_dtype logits_dtype) {
+static size_t workspace_size(int32_t batch, int32_t total_draft_tokens, int32_t max_k, int32_t vocab,
+                             rs_dtype logits_dtype, bool filtered) {
   if (logits_dtype != RS_F32 && logits_dtype != RS_BF16) return 0;
   if (batch == 0 && total_draft_tokens == 0 && vocab >= 1 && max_k >= 0 && max_k <= RS_MAX_SPEC_LEN) return 0;
   if (!rsv::sizes_ok(batch, total_draft_tokens, max_k, vocab)) return 0;
   rsv::Plan p;
-  if (!rsv::make_plan(batch, total_draft_tokens, max_k, vocab, logits_dtype, nullptr, false, p)) return 0;
+  if (!rsv::make_plan(batch, total_draft_tokens, max_k, vocab, logits_dtype, nullptr, filtered, p)) return 0;
   return p.total;
+}
+
+size_t rs_verify_workspace_size(int32_t batch, int32_t total_draft_tokens, int32_t max_k, int32_t vocab,
+                                rs_dtype logits_dtype) {
+  return workspace_size(batch, total_draft_tokens, max_k, vocab, logits_dtype, false);
+}
+
+size_t rs_verify_filtered_workspace_size(int32_t batch, int32_t total_draft_tokens, int32_t max_k, int32_t vocab,
+                                         rs_dtype logits_dtype) {
+  return workspace_size(batch, total_draft_tokens, max_k, vocab, logits_dtype, true);
 }
 
 rs_status rs_verify(const void* target_logits, rs_dtype logits_dtype, const float* draft_probs,

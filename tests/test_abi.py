@@ -28,7 +28,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert _declared_functions() == ["rs_abi_version", "rs_status_string", "rs_verify", "rs_verify_filtered",
-                                     "rs_verify_greedy", "rs_verify_workspace_size"]
+                                     "rs_verify_filtered_workspace_size", "rs_verify_greedy",
+                                     "rs_verify_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -59,6 +60,10 @@ def test_workspace_size(lib):
     assert lib.rs_verify_workspace_size(2, 4, 4, 10, 5) == 0      # dtype
     # grows with the batch
     assert rs.workspace_size(512, 4096, 8, 151936) > n
+    # the filtered entry point adds one fp32 maximum per 4096-byte row segment
+    nf = rs.workspace_size(256, 2048, 8, 151936, filtered=True)
+    assert nf >= n + 2304 * 5 * 256 * 4
+    assert lib.rs_verify_filtered_workspace_size(2, 9, 4, 10, 1) == 0
 
 
 def _gpu_present():

@@ -40,8 +40,8 @@ def _mixed_filters(w, seed):
     return w.with_filters(top_k.tolist(), top_p.tolist())
 
 
-def _case(name, ks, V, dtype, q_mode, temp, seed, ties=False):
-    w = W.make(ks, V, dtype=dtype, logit_std=3.0, temperature=temp, q_mode=q_mode, q_sigma=0.8,
+def _case(name, ks, V, dtype, q_mode, temp, seed, ties=False, std=3.0):
+    w = W.make(ks, V, dtype=dtype, logit_std=std, temperature=temp, q_mode=q_mode, q_sigma=0.8,
                draft_mode="sample_q" if q_mode == "noise" else "argmax_mix", seed=seed, gen_seed=6000 + seed,
                device="cuda", name=name)
     if ties:  # few distinct logit values: ties at every threshold
@@ -60,7 +60,17 @@ CASES = [
                                          ties=True)),
     ("fp32 onehot ties V=777", lambda: _case("fp32 onehot ties V=777", [2] * 30, 777, torch.float32, "none", 0.8,
                                              25, ties=True)),
+    # Nearly flat targets: top-p keeps tens of thousands of tokens (selection
+    # over the whole row).  Each token then moves the cumulative mass by
+    # ~1e-5 of the total, so the top-p boundary falls within the 1e-6 near-tie
+    # band of the target on ~10% of rows; the oracle flags those rows, and
+    # only the unflagged ones must match.
+    ("bf16 q flat V=151936", lambda: _case("bf16 q flat V=151936", [3] * 16, 151936, torch.bfloat16, "noise", 2.0,
+                                           28, std=0.3)),
+    ("fp32 q flat V=100000", lambda: _case("fp32 q flat V=100000", [2] * 12, 100000, torch.float32, "noise", 1.5,
+                                           29, std=0.5)),
 ]
+MAX_FLAGGED = {"bf16 q flat V=151936": 4, "fp32 q flat V=100000": 4}
 
 
 @pytest.mark.parametrize("name,build", CASES, ids=[c[0] for c in CASES])
@@ -72,7 +82,7 @@ def test_filtered_parity(name, build):
     rep = compare(g, o, w)
     worst = compare_p(g, o)
     _say(f"{name}: flagged {rep['flagged']}/{rep['requests']}, max p' rel err {worst:.3e}")
-    assert rep["flagged"] <= 1
+    assert rep["flagged"] <= MAX_FLAGGED.get(name, 1)
 
 
 @pytest.mark.parametrize("n", [4, 5, 2])

@@ -200,15 +200,20 @@ def main():
 
     ends = tuple(int(x) for x in args.phases.split(",") if x.strip())
 
+    filt = {"top_k": None, "top_p": None}  # set while timing the filtered variants
+    ws_f = None
+
     def call(i, debug=None):
         w = copies[i]
         if debug is None and ends:
             debug = rs.Debug(phase_ends=ends)
         elif debug is not None and ends and not debug.phase_ends:
             debug.phase_ends = ends
+        tk, tp = filt["top_k"], filt["top_p"]
         rs.verify(w.logits, w.draft_probs, w.draft_token_ids, w.cu_num_draft_tokens, w.temperature,
-                  seed=w.seed, max_k=w.max_k, out=outs[i], num_accepted=naccs[i], workspace=ws, debug=debug,
-                  stream=stream)
+                  seed=w.seed, max_k=w.max_k, out=outs[i], num_accepted=naccs[i],
+                  workspace=ws if tk is None and tp is None else ws_f, debug=debug, stream=stream,
+                  top_k=tk, top_p=tp)
 
     # Warm-up runs straight into the timed region (the GPU's clocks drop after
     # even a few milliseconds idle), with no garbage-collection pauses on the
@@ -328,6 +333,21 @@ def main():
         for split in ((1,), (2,), (3,), (4,), (5,), (1, 3), (2, 4), (2, 5), (3, 5), (1, 2, 4), (1, 3, 5), (2, 3, 5)):
             ms_v = timed_steps(phase_ends=split)
             log(f"phase ends {split}: {ms_v * 1e3:.1f} us/step, {w0.D / (ms_v / 1e3):.3g} positions/s")
+    # top-k / top-p filtered verify (rs_verify_filtered) on the same inputs:
+    # every request with top_k = 50 and top_p = 0.9, or one of them
+    ws_f = torch.zeros(max(rs.workspace_size(w.B, w.D, w.max_k, w.V, w.logits.dtype, filtered=True) for w in copies),
+                       dtype=torch.uint8, device=dev)
+    for name, k, p in (("filtered_topk50_topp0.9", 50, 0.9), ("filtered_topk50", 50, None),
+                       ("filtered_topp0.9", None, 0.9)):
+        filt["top_k"] = None if k is None else torch.full((w0.B,), k, dtype=torch.int32, device=dev)
+        filt["top_p"] = None if p is None else torch.full((w0.B,), p, dtype=torch.float32, device=dev)
+        ms_v = timed_steps()
+        tk = kernel_times()
+        variants[name] = {"ms_per_step": ms_v, "positions_per_s": w0.D / (ms_v / 1e3),
+                          "kernel_us": [round(x * 1e3, 1) for x in tk]}
+        log(f"{name}: {ms_v * 1e3:.1f} us/step, {w0.D / (ms_v / 1e3):.3g} positions/s; kernels (us) "
+            f"{variants[name]['kernel_us']}")
+    filt["top_k"] = filt["top_p"] = None
     tv = kernel_times(sampling_path=2, phase_ends=(-1,))
     lg = (w0.D + w0.B) * w0.V * w0.logits.element_size()
     variants["one_phase_every_row"]["row_pass_us"] = tv[0] * 1e3

@@ -348,6 +348,22 @@ def main():
         log(f"{name}: {ms_v * 1e3:.1f} us/step, {w0.D / (ms_v / 1e3):.3g} positions/s; kernels (us) "
             f"{variants[name]['kernel_us']}")
     filt["top_k"] = filt["top_p"] = None
+    for i in range(args.copies):  # the unfiltered outcome of every copy again
+        call(i)
+    # acceptance counters after each call (rs_accept_stats_accumulate), one launch per step
+    counters = torch.zeros(rs.STATS_COUNTERS, dtype=torch.int64, device=dev)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s0.record(stream)
+    for k in range(args.steps):
+        rs.accept_stats_accumulate(naccs[k % args.copies], copies[k % args.copies].cu_num_draft_tokens, counters,
+                                   stream=stream)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    variants["accept_stats"] = {"us_per_step": s0.elapsed_time(s1) / args.steps * 1e3,
+                                "accept_rate": rs.accept_rate(counters), "accept_length": rs.accept_length(counters)}
+    log(f"accept_stats: {variants['accept_stats']['us_per_step']:.1f} us/step; alpha "
+        f"{variants['accept_stats']['accept_rate']:.4f}, tau {variants['accept_stats']['accept_length']:.4f}")
     tv = kernel_times(sampling_path=2, phase_ends=(-1,))
     lg = (w0.D + w0.B) * w0.V * w0.logits.element_size()
     variants["one_phase_every_row"]["row_pass_us"] = tv[0] * 1e3

@@ -205,6 +205,41 @@ rs_status rs_verify_greedy(const void* target_logits, rs_dtype logits_dtype,
                            int32_t* output_token_ids, int32_t* num_accepted, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
+/* ---- Acceptance statistics ------------------------------------------------
+ * Running counters a serving engine exports per verify step: draft proposals
+ * (requests that proposed at least one draft -- proposals, not tokens),
+ * proposed draft tokens, accepted draft tokens and accepted tokens per draft
+ * position [第12章 §12.7.5]; acceptance rate = accepted / proposed (bonus
+ * excluded) and acceptance length = emitted tokens / verifies, every verify
+ * emitting its accepted drafts plus one extra token
+ * [投机解码（Speculative Decoding）端到端深挖 §13].  One verify is one request
+ * in one step; requests with num_accepted = -1 (invalid) are not counted. */
+#define RS_STATS_SCALARS 5
+#define RS_STATS_COUNTERS (RS_STATS_SCALARS + RS_MAX_SPEC_LEN)
+/* counters[] layout (int64):
+ *   [0] draft proposals      [1] proposed draft tokens   [2] accepted draft tokens
+ *   [3] emitted tokens       [4] verifies
+ *   [RS_STATS_SCALARS + j]   requests whose drafts 0 .. j were all accepted, j < 32 */
+
+/* Adds one verify step's outcome to the counters, asynchronously on `stream`
+ * (call it after rs_verify* on the same stream).
+ *   num_accepted        [B] int32 device: rs_verify*'s output
+ *   cu_num_draft_tokens [B+1] int32 device: the same prefix sums as the call
+ *   counters            [RS_STATS_COUNTERS] int64 device, 8-byte aligned, owned by
+ *                       the caller, zeroed by the caller to start; accumulated
+ *                       with device atomics (calls may overlap)
+ * batch = 0 returns RS_OK without touching the GPU; NULL pointers or B < 0:
+ * RS_ERR_INVALID_ARG; misalignment: RS_ERR_UNSUPPORTED; a failed launch:
+ * RS_ERR_HIP.  All checks run before the launch. */
+rs_status rs_accept_stats_accumulate(const int32_t* num_accepted, const int32_t* cu_num_draft_tokens,
+                                     int32_t batch, int64_t* counters, hipStream_t stream);
+
+/* alpha = accepted / proposed draft tokens and tau = emitted tokens /
+ * verifies from a HOST copy of the counters; NaN when the denominator is 0
+ * or the pointer is NULL. */
+double rs_accept_rate(const int64_t* counters);
+double rs_accept_length(const int64_t* counters);
+
 /* Static string naming a status. */
 const char* rs_status_string(rs_status status);
 

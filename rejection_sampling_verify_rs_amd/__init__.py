@@ -19,10 +19,13 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 __all__ = ["verify", "verify_greedy", "workspace_size", "Debug", "RsVerifyError", "load_library",
-           "MAX_SPEC_LEN", "LIB_PATH"]
+           "accept_stats_accumulate", "accept_rate", "accept_length", "MAX_SPEC_LEN", "STATS_COUNTERS",
+           "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librs_verify.so")
 MAX_SPEC_LEN = 32
+STATS_SCALARS = 5
+STATS_COUNTERS = STATS_SCALARS + MAX_SPEC_LEN
 
 RS_OK, RS_ERR_INVALID_ARG, RS_ERR_UNSUPPORTED, RS_ERR_WORKSPACE, RS_ERR_HIP = range(5)
 RS_F32, RS_BF16 = 0, 1
@@ -72,6 +75,12 @@ def load_library(path: str = LIB_PATH):
     lib.rs_verify_filtered.restype = ctypes.c_int
     lib.rs_verify_greedy.argtypes = [P, ctypes.c_int, P, P, i32, i32, i32, i32, P, P, P, sz, P]
     lib.rs_verify_greedy.restype = ctypes.c_int
+    lib.rs_accept_stats_accumulate.argtypes = [P, P, i32, P, P]
+    lib.rs_accept_stats_accumulate.restype = ctypes.c_int
+    lib.rs_accept_rate.argtypes = [P]
+    lib.rs_accept_rate.restype = ctypes.c_double
+    lib.rs_accept_length.argtypes = [P]
+    lib.rs_accept_length.restype = ctypes.c_double
     lib.rs_status_string.argtypes = [ctypes.c_int]
     lib.rs_status_string.restype = ctypes.c_char_p
     lib.rs_abi_version.argtypes = []
@@ -249,3 +258,49 @@ def verify_greedy(target_logits: torch.Tensor, draft_token_ids: torch.Tensor, cu
         workspace.data_ptr(), workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
     _check(status)
     return out, num_accepted
+
+
+def accept_stats_accumulate(num_accepted: torch.Tensor, cu_num_draft_tokens: torch.Tensor,
+                            counters: Optional[torch.Tensor] = None,
+                            stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Add one verify step to the running acceptance counters
+    (rs_accept_stats_accumulate); counters is an int64 [STATS_COUNTERS] device
+    tensor (created zeroed when None).  Returns counters."""
+    lib = load_library()
+    if not isinstance(num_accepted, torch.Tensor) or num_accepted.device.type != "cuda":
+        raise ValueError("num_accepted must be a CUDA (HIP) tensor")
+    dev = num_accepted.device
+    _dev_tensor(num_accepted, "num_accepted", torch.int32, dev)
+    _dev_tensor(cu_num_draft_tokens, "cu_num_draft_tokens", torch.int32, dev)
+    B = int(num_accepted.numel())
+    if cu_num_draft_tokens.numel() != B + 1:
+        raise ValueError("cu_num_draft_tokens needs B + 1 entries")
+    if counters is None:
+        counters = torch.zeros(STATS_COUNTERS, dtype=torch.int64, device=dev)
+    _dev_tensor(counters, "counters", torch.int64, dev)
+    if counters.numel() != STATS_COUNTERS:
+        raise ValueError(f"counters must hold {STATS_COUNTERS} int64 values")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    _check(lib.rs_accept_stats_accumulate(num_accepted.data_ptr(), cu_num_draft_tokens.data_ptr(), B,
+                                          counters.data_ptr(), ctypes.c_void_p(stream.cuda_stream)))
+    return counters
+
+
+def _host_counters(counters) -> "torch.Tensor":
+    c = counters.detach().to("cpu", torch.int64).contiguous()
+    if c.numel() != STATS_COUNTERS:
+        raise ValueError(f"counters must hold {STATS_COUNTERS} int64 values")
+    return c
+
+
+def accept_rate(counters) -> float:
+    """alpha = accepted / proposed draft tokens (rs_accept_rate on a host copy)."""
+    c = _host_counters(counters)
+    return float(load_library().rs_accept_rate(c.data_ptr()))
+
+
+def accept_length(counters) -> float:
+    """tau = emitted tokens / verifies (rs_accept_length on a host copy)."""
+    c = _host_counters(counters)
+    return float(load_library().rs_accept_length(c.data_ptr()))

@@ -37,6 +37,7 @@
 #include "row_pass.hpp"
 #include "rs_verify.h"
 #include "scan.hpp"
+#include "stats.hpp"
 #include "stream_path.hpp"
 
 namespace rsv {
@@ -591,6 +592,27 @@ rs_status rs_verify_greedy(const void* target_logits, rs_dtype logits_dtype, con
   return rsv::verify_impl(target_logits, logits_dtype, nullptr, draft_token_ids, cu_num_draft_tokens, nullptr,
                           nullptr, nullptr, 1, batch, total_draft_tokens, max_k, vocab, 0, output_token_ids,
                           num_accepted, workspace, workspace_bytes, nullptr, stream);
+}
+
+rs_status rs_accept_stats_accumulate(const int32_t* num_accepted, const int32_t* cu_num_draft_tokens, int32_t batch,
+                                     int64_t* counters, hipStream_t stream) {
+  if (batch < 0) return RS_ERR_INVALID_ARG;
+  if (batch == 0) return RS_OK;
+  if (!num_accepted || !cu_num_draft_tokens || !counters) return RS_ERR_INVALID_ARG;
+  if (((uintptr_t)num_accepted % 4) || ((uintptr_t)cu_num_draft_tokens % 4) || ((uintptr_t)counters % 8))
+    return RS_ERR_UNSUPPORTED;
+  const unsigned grid = (unsigned)((batch + rsv::kStatsThreads - 1) / rsv::kStatsThreads);
+  rsv::stats_kernel<<<grid, rsv::kStatsThreads, 0, stream>>>(num_accepted, cu_num_draft_tokens, batch,
+                                                              reinterpret_cast<unsigned long long*>(counters));
+  return hipGetLastError() == hipSuccess ? RS_OK : RS_ERR_HIP;
+}
+
+double rs_accept_rate(const int64_t* c) {
+  return (c && c[1] > 0) ? (double)c[2] / (double)c[1] : __builtin_nan("");
+}
+
+double rs_accept_length(const int64_t* c) {
+  return (c && c[4] > 0) ? (double)c[3] / (double)c[4] : __builtin_nan("");
 }
 
 const char* rs_status_string(rs_status status) {

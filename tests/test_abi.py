@@ -27,8 +27,9 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["rs_abi_version", "rs_status_string", "rs_verify", "rs_verify_filtered",
-                                     "rs_verify_filtered_workspace_size", "rs_verify_greedy",
+    assert _declared_functions() == ["rs_abi_version", "rs_accept_length", "rs_accept_rate",
+                                     "rs_accept_stats_accumulate", "rs_status_string", "rs_verify",
+                                     "rs_verify_filtered", "rs_verify_filtered_workspace_size", "rs_verify_greedy",
                                      "rs_verify_workspace_size"]
 
 
@@ -190,3 +191,31 @@ def test_filtered_entry_validation(lib, kw, status):
 @needs_no_gpu
 def test_filtered_entry_empty_batch(lib):
     assert _call_filtered(lib, B=0, D=0, logits=None, out=None, nacc=None, ws=None) == rs.RS_OK
+
+
+@needs_no_gpu
+def test_stats_entry_validation(lib):
+    f = lib.rs_accept_stats_accumulate
+    assert f(DUMMY, DUMMY, -1, DUMMY, None) == rs.RS_ERR_INVALID_ARG
+    assert f(None, DUMMY, 4, DUMMY, None) == rs.RS_ERR_INVALID_ARG
+    assert f(DUMMY, None, 4, DUMMY, None) == rs.RS_ERR_INVALID_ARG
+    assert f(DUMMY, DUMMY, 4, None, None) == rs.RS_ERR_INVALID_ARG
+    assert f(DUMMY, DUMMY, 4, DUMMY + 4, None) == rs.RS_ERR_UNSUPPORTED
+    assert f(None, None, 0, None, None) == rs.RS_OK
+
+
+def test_stats_host_helpers(lib):
+    import json
+    import numpy as np
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "accept_stats_worked_example.json")))
+    c = np.zeros(rs.STATS_COUNTERS, np.int64)
+    c[1] = g["verifies"] * g["K"]
+    c[2] = g["accepted_total"]
+    c[3] = g["completion_tokens"]
+    c[4] = g["verifies"]
+    p = c.ctypes.data_as(ctypes.c_void_p)
+    assert lib.rs_accept_rate(p) == g["accept_rate"]
+    assert lib.rs_accept_length(p) == g["accept_length"]
+    import math
+    assert math.isnan(lib.rs_accept_rate(np.zeros(rs.STATS_COUNTERS, np.int64).ctypes.data_as(ctypes.c_void_p)))
+    assert math.isnan(lib.rs_accept_length(None))

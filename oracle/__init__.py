@@ -63,6 +63,8 @@ def _load():
     lib.rso_verify_filtered.restype = ctypes.c_int
     lib.rso_filtered_probs_row.argtypes = [P, i32, f64, i32, f64, f64, P, P, P]
     lib.rso_filtered_probs_row.restype = None
+    lib.rso_verify_tree.argtypes = [P, i32, P, P, P, P, i32, i32, i32, i32, i32, u64, f64, P, P, P, P, i32]
+    lib.rso_verify_tree.restype = ctypes.c_int
     lib.rso_probs.argtypes = [P, i32, P, P, i32, i32, P]
     lib.rso_probs.restype = ctypes.c_int
     lib.rso_softmax_row.argtypes = [P, i32, f64, P]
@@ -153,6 +155,45 @@ def verify(logits, draft_probs, draft_token_ids, cu_num_draft_tokens, temperatur
     if rc != 0:
         raise RuntimeError("oracle rejected its arguments")
     return OracleResult(out, nacc, flags, pd)
+
+
+@dataclass
+class TreeResult:
+    tokens: np.ndarray        # [B, max_depth + 1] int32, -1 padded
+    path: np.ndarray          # [B, max_depth] accepted node indices (request-local), -1 padded
+    num_accepted: np.ndarray  # [B] int32
+    flags: np.ndarray         # [B] int32
+
+    @property
+    def near_tie(self) -> np.ndarray:
+        return (self.flags & NEAR_TIE_FLAGS) != 0
+
+
+def verify_tree(logits, node_tokens, node_parents, cu_num_nodes, temperature, seed: int, max_nodes: int,
+                max_depth: int, *, eps: float = DEFAULT_EPS, threads: int = 0) -> TreeResult:
+    """Tree verify (rs_oracle.c, rso_verify_tree): request b's rows start at
+    cu[b] + b (row 0 the root position, row 1 + i node i)."""
+    lib = _load()
+    lg, code = _logits_arg(logits)
+    V = int(lg.shape[-1])
+    tok = _to_numpy(node_tokens, np.int32)
+    par = _to_numpy(node_parents, np.int32)
+    cu = _to_numpy(cu_num_nodes, np.int32)
+    T = _to_numpy(temperature, np.float32)
+    B = int(cu.shape[0]) - 1
+    N = int(tok.shape[0])
+    if lg.size != (N + B) * V:
+        raise ValueError("logits must hold N + B rows")
+    out = np.empty((B, max_depth + 1), np.int32)
+    path = np.empty((B, max(max_depth, 0)), np.int32)
+    nacc = np.empty(B, np.int32)
+    flags = np.empty(B, np.int32)
+    rc = lib.rso_verify_tree(_ptr(lg), code, _ptr(tok), _ptr(par), _ptr(cu), _ptr(T), B, N, int(max_nodes),
+                             int(max_depth), V, int(seed) & ((1 << 64) - 1), float(eps), _ptr(out), _ptr(path),
+                             _ptr(nacc), _ptr(flags), int(threads))
+    if rc != 0:
+        raise RuntimeError("oracle rejected its arguments")
+    return TreeResult(out, path, nacc, flags)
 
 
 def verify_greedy(logits, draft_token_ids, cu_num_draft_tokens, max_k: int,

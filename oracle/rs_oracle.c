@@ -447,6 +447,148 @@ int rso_verify(const void* logits, int32_t dtype, const float* q, const int32_t*
                              eps, out, num_accepted, flags, p_draft, nthreads);
 }
 
+/* ------------------------------------------------------------------------ */
+/* Tree verify.  A request's drafts form a tree (each node one draft token,
+ * its parent earlier in the node order or -1 for a child of the last prefix
+ * position); the target scored the last prefix position (row 0) and every
+ * node (row 1 + i), row r predicting the children of its node.  Verification
+ * walks the tree from the root one depth at a time and stops at the first
+ * depth where no child is accepted; one extra token is then emitted from the
+ * stop node's row.  [投机解码深度实战 §四 (tree drafts, one forward over the
+ * whole tree); 投机解码（Speculative Decoding）端到端深挖 §6.2 (per depth, match
+ * among the current layer's siblings, descend into the match, stop when the
+ * whole layer fails; a bonus follows the last accepted node), §7.1 (greedy),
+ * §7.2 (random: one coin per layer against the siblings' accumulated target
+ * probabilities; the extra token from the residual)]
+ *   greedy (T <= 0): the child whose token is the row's argmax (lowest index
+ *     on ties, first such child), else stop and emit the argmax.
+ *   random: p = softmax(row / T); coin u_d = the accept uniform of depth d;
+ *     children in node order, a child whose token repeats an earlier
+ *     sibling's is skipped; child i is accepted iff u_d < (sum of p over the
+ *     siblings up to and including i); if none, emit the race over p with
+ *     the children's tokens removed (exponentials of depth d); a node
+ *     without children emits the race over p (the bonus).
+ * Reading (§7.2 with both thresholds at their default 1.0 and the draft
+ * distribution one-hot on the siblings): each sibling is accepted with
+ * probability p(its token) and the residual is p without the siblings, so the
+ * emitted token at every depth is distributed as p.  A one-child-per-node tree
+ * is the chain with one-hot q, with the same random numbers.
+ *   tree tokens [N], parents [N] (request-local node index or -1), cu [B+1];
+ *   out [B, max_depth + 1] tokens (-1 padded), path [B, max_depth] node
+ *   indices (-1 padded), num_accepted [B]; flags as rso_verify (invalid:
+ *   parent >= node or < -1, token outside [0, V), depth beyond max_depth,
+ *   more than max_nodes nodes).
+ * Returns 0, or -1 on an argument error. */
+int rso_verify_tree(const void* logits, int32_t dtype, const int32_t* tokens, const int32_t* parents,
+                    const int32_t* cu, const float* T, int32_t B, int32_t N, int32_t max_nodes, int32_t max_depth,
+                    int32_t V, uint64_t seed, double eps, int32_t* out, int32_t* path, int32_t* num_accepted,
+                    int32_t* flags, int32_t nthreads) {
+  if (!logits || !cu || !T || !out || !path || !num_accepted || !flags) return -1;
+  if (B < 0 || N < 0 || V < 1 || max_nodes < 0 || max_depth < 0 || (N > 0 && (!tokens || !parents))) return -1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* l = (double*)malloc(sizeof(double) * (size_t)V);
+    double* p = (double*)malloc(sizeof(double) * (size_t)V);
+    double* r = (double*)malloc(sizeof(double) * (size_t)V);
+    double* rlo = (double*)malloc(sizeof(double) * (size_t)V);
+    double* rhi = (double*)malloc(sizeof(double) * (size_t)V);
+    double* E = (double*)malloc(sizeof(double) * (size_t)V);
+    int32_t* depth = (int32_t*)malloc(sizeof(int32_t) * (size_t)(max_nodes > 0 ? max_nodes : 1));
+    if (!l || !p || !r || !rlo || !rhi || !E || !depth) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int32_t b = 0; b < B; ++b) {
+      if (failed) continue;
+      int32_t* ob = out + (int64_t)b * (max_depth + 1);
+      int32_t* pb = path + (int64_t)b * max_depth;
+      for (int32_t i = 0; i <= max_depth; ++i) ob[i] = -1;
+      for (int32_t i = 0; i < max_depth; ++i) pb[i] = -1;
+      num_accepted[b] = -1;
+      flags[b] = 0;
+      int32_t s = cu[b], e = cu[b + 1], n = e - s;
+      int valid = (s >= 0 && e <= N && n >= 0 && n <= max_nodes);
+      for (int32_t i = 0; valid && i < n; ++i) {
+        int32_t par = parents[s + i];
+        if (par < -1 || par >= i || tokens[s + i] < 0 || tokens[s + i] >= V) valid = 0;
+        else {
+          depth[i] = par < 0 ? 0 : depth[par] + 1;
+          if (depth[i] >= max_depth) valid = 0;
+        }
+      }
+      if (!valid) {
+        flags[b] = RSO_FLAG_INVALID;
+        continue;
+      }
+      int64_t row0 = (int64_t)s + b; /* root row; node i is row row0 + 1 + i */
+      int greedy = !(T[b] > 0.0f);
+      double Tb = (double)T[b];
+      int32_t cur = -1, d = 0, token = -1;
+      for (;;) {
+        load_row(logits, dtype, row0 + 1 + cur, V, l);
+        int32_t next = -1;
+        if (greedy) {
+          int32_t g = argmax_lowest(l, V);
+          for (int32_t i = 0; i < n && next < 0; ++i)
+            if (parents[s + i] == cur && tokens[s + i] == g) next = i;
+          if (next < 0) token = g;
+        } else {
+          rso_softmax_row(l, V, Tb, p);
+          double u = rso_accept_uniform(seed, b, d), cum = 0.0;
+          for (int32_t i = 0; i < n && next < 0; ++i) {
+            if (parents[s + i] != cur) continue;
+            int dup = 0;
+            for (int32_t k = 0; k < i; ++k)
+              if (parents[s + k] == cur && tokens[s + k] == tokens[s + i]) dup = 1;
+            if (dup) continue;
+            cum += p[tokens[s + i]];
+            if (fabs(u - cum) <= eps * cum) flags[b] |= RSO_FLAG_ACCEPT_TIE;
+            if (u < cum) next = i;
+          }
+          if (next < 0) {
+            /* residual: p without the children's tokens (a childless node: p) */
+            for (int32_t x = 0; x < V; ++x) r[x] = p[x];
+            for (int32_t i = 0; i < n; ++i)
+              if (parents[s + i] == cur) r[tokens[s + i]] = 0.0;
+            for (int32_t x = 0; x < V; ++x) {
+              rlo[x] = r[x] * (1.0 - eps);
+              rhi[x] = r[x] * (1.0 + eps);
+            }
+            int tie = 0;
+            token = race(r, rlo, rhi, V, seed, b, d, eps, E, &tie);
+            if (token < 0) { /* every token drafted: race over p */
+              flags[b] |= RSO_FLAG_ZERO_RESIDUAL;
+              for (int32_t x = 0; x < V; ++x) {
+                r[x] = p[x];
+                rlo[x] = p[x] * (1.0 - eps);
+                rhi[x] = p[x] * (1.0 + eps);
+              }
+              token = race(r, rlo, rhi, V, seed, b, d, eps, E, &tie);
+            }
+            if (tie) flags[b] |= RSO_FLAG_RACE_TIE;
+          }
+        }
+        if (next < 0) break;
+        ob[d] = tokens[s + next];
+        pb[d] = next;
+        cur = next;
+        ++d;
+      }
+      ob[d] = token;
+      num_accepted[b] = d;
+    }
+    free(l); free(p); free(r); free(rlo); free(rhi); free(E); free(depth);
+  }
+  return failed ? -1 : 0;
+}
+
 /* Full p = softmax(l / T_b) for every row of every request (rows of greedy
  * requests, T <= 0, are filled with NaN).  Used to check the library's
  * optional full-probability output on small shapes. */

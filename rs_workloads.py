@@ -235,3 +235,101 @@ def config(n: int, device="cpu", copy: int = 0, *, B: Optional[int] = None,
                     seed=VERIFY_SEED[5], gen_seed=gs, device=device,
                     name="B=512 K=3 V=129280 bf16")
     raise ValueError(f"no workload {n}")
+
+
+@dataclass
+class TreeWorkload:
+    """A batch of draft trees.  Request b has cu[b+1] - cu[b] nodes (node
+    order: every parent before its children); its logits rows start at
+    cu[b] + b: row 0 scores the last prefix position (predicts the root's
+    children), row 1 + i scores node i (predicts node i's children)."""
+    name: str
+    logits: torch.Tensor          # [N + B, V]
+    node_tokens: torch.Tensor     # [N] int32
+    node_parents: torch.Tensor    # [N] int32, request-local, -1 = child of the prefix
+    cu_num_nodes: torch.Tensor    # [B + 1] int32
+    temperature: torch.Tensor     # [B] fp32, <= 0 greedy
+    seed: int
+    num_nodes: List[int] = field(default_factory=list)
+    max_depth: int = 0
+
+    @property
+    def B(self) -> int:
+        return len(self.num_nodes)
+
+    @property
+    def N(self) -> int:
+        return int(sum(self.num_nodes))
+
+    @property
+    def V(self) -> int:
+        return int(self.logits.shape[-1])
+
+    @property
+    def max_nodes(self) -> int:
+        return max(self.num_nodes) if self.num_nodes else 0
+
+    def to(self, device) -> "TreeWorkload":
+        return TreeWorkload(self.name, self.logits.to(device), self.node_tokens.to(device),
+                            self.node_parents.to(device), self.cu_num_nodes.to(device), self.temperature.to(device),
+                            self.seed, list(self.num_nodes), self.max_depth)
+
+
+def tree_shape(depth: int, branching: Sequence[int], max_nodes: int) -> List[int]:
+    """Parents of a breadth-first tree: each node of depth d < depth gets
+    branching[d] children, truncated at max_nodes nodes."""
+    parents: List[int] = []
+    frontier = [-1]
+    for d in range(depth):
+        nxt = []
+        for par in frontier:
+            for _ in range(branching[d]):
+                if len(parents) >= max_nodes:
+                    return parents
+                parents.append(par)
+                nxt.append(len(parents) - 1)
+        frontier = nxt
+    return parents
+
+
+def make_tree(B: int, V: int, *, depth: int = 5, branching=(4, 2, 2, 1, 1), max_nodes: int = 64,
+              dtype=torch.bfloat16, logit_std: float = 4.0, temperature=1.0, draft_noise: float = 1.0,
+              seed: int = 0, gen_seed: int = 2000, device="cpu", name: str = "tree") -> TreeWorkload:
+    """EAGLE-style draft trees: every request has the same shape (tree_shape);
+    the children of a node are the top tokens of (that node's target row / T
+    + N(0, draft_noise^2)), which is how a draft model that roughly agrees with
+    the target proposes them."""
+    device = torch.device(device)
+    g = _gen(device, gen_seed)
+    parents = tree_shape(depth, list(branching), max_nodes)
+    n = len(parents)
+    R = B * (n + 1)
+    logits = (torch.randn(R, V, generator=g, device=device, dtype=torch.float32) * logit_std).to(dtype)
+    widened = logits.to(torch.float32)
+    if isinstance(temperature, tuple) and temperature[0] == "uniform":
+        T = temperature[1] + (temperature[2] - temperature[1]) * torch.rand(B, generator=g, device=device)
+    elif isinstance(temperature, (list, tuple, torch.Tensor)):
+        T = torch.as_tensor(temperature, dtype=torch.float32).to(device)
+    else:
+        T = torch.full((B,), float(temperature), dtype=torch.float32, device=device)
+    par = torch.tensor(parents, dtype=torch.int32)
+    tokens = torch.empty(B, n, dtype=torch.int32)
+    Tc = T.cpu()
+    for b in range(B):
+        base = b * (n + 1)
+        for node_row in range(-1, n):
+            kids = [i for i in range(n) if parents[i] == node_row]
+            if not kids:
+                continue
+            Tb = float(Tc[b]) if float(Tc[b]) > 0 else 1.0
+            row = widened[base + 1 + node_row] / Tb
+            noisy = row + draft_noise * torch.randn(V, generator=g, device=device)
+            top = torch.topk(noisy, len(kids)).indices.cpu()
+            for k, i in enumerate(kids):
+                tokens[b, i] = int(top[k])
+    cu = torch.arange(B + 1, dtype=torch.int32) * n
+    depth_of = []
+    for i, p_ in enumerate(parents):
+        depth_of.append(0 if p_ < 0 else depth_of[p_] + 1)
+    return TreeWorkload(name, logits.contiguous(), tokens.reshape(-1).to(device), par.repeat(B).to(device),
+                        cu.to(device), T.contiguous(), int(seed), [n] * B, (max(depth_of) + 1) if depth_of else 0)

@@ -1,0 +1,145 @@
+"""Pins of the oracle's tree verify (rso_verify_tree) [投机解码深度实战 §四;
+投机解码（Speculative Decoding）端到端深挖 §6.2, §7.1, §7.2]:
+
+ - the greedy walks the pages draw (tests/golden/tree_worked_examples.json);
+ - a one-child-per-node tree is the chain: tokens and counts equal the chain
+   oracle with one-hot q (same random numbers), greedy and random;
+ - exact law of one layer: with siblings s_1..s_m the walk accepts s_i with
+   probability p(s_i) and otherwise emits the residual p without the
+   siblings, so the first emitted token follows p (chi-square, 10^6 trials);
+   after accepting s_i the bonus follows that node's row; a repeated sibling
+   token is skipped and the law still holds;
+ - greedy against brute force (numpy argmax walk) on random trees;
+ - invalid trees (parent after its child, token out of range, too deep).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+from scipy import special, stats
+
+import oracle
+import rs_workloads as W
+
+PVAL = 1e-3
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "tree_worked_examples.json")
+
+
+def _rows_from_argmax(argmax, V=8):
+    rows = np.zeros((len(argmax), V), np.float32)
+    for r, a in enumerate(argmax):
+        rows[r, a] = 5.0
+    return rows
+
+
+def test_greedy_worked_examples():
+    for c in json.load(open(GOLDEN))["cases"]:
+        lg = _rows_from_argmax(c["argmax"])
+        n = len(c["tokens"])
+        r = oracle.verify_tree(lg, np.array(c["tokens"], np.int32), np.array(c["parents"], np.int32),
+                               np.array([0, n], np.int32), np.array([0.0], np.float32), 0, n, 3)
+        assert r.num_accepted[0] == c["num_accepted"], c["cite"]
+        k = c["num_accepted"]
+        assert r.path[0, :k].tolist() == c["path"]
+        assert r.tokens[0, :k + 1].tolist() == c["out"]
+        assert (r.tokens[0, k + 1:] == -1).all() and (r.path[0, k:] == -1).all()
+
+
+@pytest.mark.parametrize("temp", [0.0, 1.0, 0.7])
+def test_chain_tree_is_the_chain(temp):
+    w = W.make([4, 0, 6, 3, 8, 1, 5, 2] * 3, 500, dtype="float32" and __import__("torch").float32,
+               temperature=temp, q_mode="none", draft_mode="argmax_mix", seed=11, gen_seed=77)
+    ks = w.num_draft
+    parents = np.concatenate([np.arange(k) - 1 for k in ks]).astype(np.int32)
+    chain = oracle.verify(w.logits, None, w.draft_token_ids, w.cu_num_draft_tokens, w.temperature, w.seed, w.max_k)
+    tree = oracle.verify_tree(w.logits, w.draft_token_ids, parents, w.cu_num_draft_tokens, w.temperature, w.seed,
+                              w.max_k, w.max_k)
+    np.testing.assert_array_equal(tree.num_accepted, chain.num_accepted)
+    np.testing.assert_array_equal(tree.tokens, chain.tokens)
+    for b, k in enumerate(ks):
+        n = tree.num_accepted[b]
+        assert tree.path[b, :n].tolist() == list(range(n))
+
+
+def _chi2(counts, probs):
+    counts = np.asarray(counts, np.float64)
+    exp = np.asarray(probs, np.float64) * counts.sum()
+    assert counts[exp == 0].sum() == 0
+    keep = exp >= 5
+    obs, ex = counts[keep], exp[keep]
+    if (~keep).any():
+        obs, ex = np.append(obs, counts[~keep].sum()), np.append(ex, exp[~keep].sum())
+    return stats.chisquare(obs, ex * obs.sum() / ex.sum()).pvalue
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("sib_tokens,T", [([5, 2, 7], 1.0), ([1, 6], 0.6), ([3, 3, 0], 1.3)])
+def test_one_layer_exact_law(sib_tokens, T):
+    V, B = 8, 1_000_000
+    rng = np.random.default_rng(sum(sib_tokens))
+    m = len(sib_tokens)
+    L = (rng.standard_normal((1 + m, V)) * 1.3).astype(np.float32)  # root row, then one row per sibling
+    p = special.softmax(L[0].astype(np.float64) / np.float32(T))
+    lg = np.ascontiguousarray(np.broadcast_to(L, (B, 1 + m, V)).reshape(B * (1 + m), V))
+    tokens = np.tile(np.array(sib_tokens, np.int32), B)
+    parents = np.full(B * m, -1, np.int32)
+    cu = (np.arange(B + 1) * m).astype(np.int32)
+    r = oracle.verify_tree(lg, tokens, parents, cu, np.full(B, T, np.float32), 123, m, 2)
+    assert r.near_tie.mean() < 1e-4
+    first = r.tokens[:, 0]
+    assert _chi2(np.bincount(first, minlength=V), p) > PVAL
+    distinct = []
+    for t in sib_tokens:
+        if t not in distinct:
+            distinct.append(t)
+    acc = r.num_accepted == 1
+    # sibling i is accepted with probability p(its token); a repeat is never taken
+    node_of = {t: sib_tokens.index(t) for t in distinct}
+    counts = [int((acc & (r.path[:, 0] == node_of[t])).sum()) for t in distinct] + [int((~acc).sum())]
+    law = [p[t] for t in distinct] + [1 - sum(p[t] for t in distinct)]
+    assert _chi2(counts, law) > PVAL
+    # the bonus after accepting sibling i follows that node's row
+    for t in distinct:
+        i = node_of[t]
+        sel = acc & (r.path[:, 0] == i)
+        if sel.sum() > 2000:
+            pi = special.softmax(L[1 + i].astype(np.float64) / np.float32(T))
+            assert _chi2(np.bincount(r.tokens[sel, 1], minlength=V), pi) > PVAL
+
+
+def test_greedy_against_brute_force():
+    import torch
+    w = W.make_tree(12, 300, depth=4, branching=(3, 2, 2, 1), max_nodes=40, dtype=torch.float32, temperature=0.0,
+                    draft_noise=0.7, gen_seed=5)
+    r = oracle.verify_tree(w.logits, w.node_tokens, w.node_parents, w.cu_num_nodes, w.temperature, 0, w.max_nodes,
+                           w.max_depth)
+    lg = w.logits.numpy()
+    tok, par = w.node_tokens.numpy(), w.node_parents.numpy()
+    n = w.max_nodes
+    for b in range(w.B):
+        base = b * (n + 1)
+        cur, path = -1, []
+        while True:
+            g = int(np.argmax(lg[base + 1 + cur]))
+            kids = [i for i in range(n) if par[b * n + i] == cur and tok[b * n + i] == g]
+            if not kids:
+                break
+            cur = kids[0]
+            path.append(cur)
+        assert r.num_accepted[b] == len(path)
+        assert r.path[b, :len(path)].tolist() == path
+        assert r.tokens[b, len(path)] == g
+
+
+def test_invalid_trees():
+    lg = np.zeros((4 * 4, 8), np.float32)
+    cu = np.array([0, 3, 6, 9, 12], np.int32)
+    tokens = np.array([1, 2, 3, 1, 2, 3, 1, 9, 3, 1, 2, 3], np.int32)
+    parents = np.array([-1, 0, 1, -1, 2, 0, -1, 0, 0, -1, 0, 1], np.int32)
+    r = oracle.verify_tree(lg, tokens, parents, cu, np.ones(4, np.float32), 0, 3, 2)
+    # request 0: depth 3 > max_depth 2; 1: parent after its child; 2: token 9 >= V; 3: depth 3 again
+    assert (r.flags & oracle.FLAG_INVALID).tolist() == [8, 8, 8, 8]
+    assert (r.num_accepted == -1).all() and (r.tokens == -1).all()
+    r = oracle.verify_tree(lg, tokens, parents, cu, np.ones(4, np.float32), 0, 3, 3)
+    assert (r.flags & oracle.FLAG_INVALID).tolist() == [0, 8, 8, 0]

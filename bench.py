@@ -364,6 +364,44 @@ def main():
                                 "accept_rate": rs.accept_rate(counters), "accept_length": rs.accept_length(counters)}
     log(f"accept_stats: {variants['accept_stats']['us_per_step']:.1f} us/step; alpha "
         f"{variants['accept_stats']['accept_rate']:.4f}, tau {variants['accept_stats']['accept_length']:.4f}")
+    # tree verify (rs_verify_tree): B=64 EAGLE-style draft trees of 60 nodes
+    # (branching 4, 2, 2, 1, 1; depth 5) at the same V, T ~ U[0.5, 1.2]
+    trees = [W.make_tree(64, w0.V, temperature=("uniform", 0.5, 1.2), seed=7, gen_seed=5000 + i, device=dev)
+             for i in range(args.copies)]
+    tw = trees[0]
+    tout = torch.empty((tw.B, tw.max_depth + 1), dtype=torch.int32, device=dev)
+    tpath = torch.empty((tw.B, tw.max_depth), dtype=torch.int32, device=dev)
+    tn = torch.empty((tw.B,), dtype=torch.int32, device=dev)
+
+    def tree_call(i):
+        t = trees[i % args.copies]
+        rs.verify_tree(t.logits, t.node_tokens, t.node_parents, t.cu_num_nodes, t.temperature, seed=t.seed,
+                       max_nodes=t.max_nodes, max_depth=t.max_depth, out=tout, accepted_nodes=tpath,
+                       num_accepted=tn, stream=stream)
+
+    for k in range(args.warmup):
+        tree_call(k)
+    torch.cuda.synchronize()
+    s0.record(stream)
+    for k in range(args.steps):
+        tree_call(k)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    tms = s0.elapsed_time(s1) / args.steps
+    rows_read = []
+    for i in range(args.copies):
+        tree_call(i)
+        torch.cuda.synchronize()
+        rows_read.append(int((tn.cpu().numpy() + 1).sum()))
+    dense = (tw.N + tw.B) * tw.V * tw.logits.element_size()
+    variants["tree_eagle_B64"] = {
+        "us_per_step": tms * 1e3, "nodes_per_s": tw.N / (tms / 1e3), "nodes": tw.N, "rows": tw.N + tw.B,
+        "rows_streamed": float(np.mean(rows_read)),
+        "effective_GBps": dense / (tms / 1e3) / 1e9}
+    log(f"tree (B=64, {tw.max_nodes} nodes, depth {tw.max_depth}): {tms * 1e3:.1f} us/step, "
+        f"{tw.N / (tms / 1e3):.3g} nodes/s, {np.mean(rows_read):.0f} of {tw.N + tw.B} rows streamed, "
+        f"{dense / (tms / 1e3) / 1e9:.0f} GB/s effective (every row once)")
+    del trees
     tv = kernel_times(sampling_path=2, phase_ends=(-1,))
     lg = (w0.D + w0.B) * w0.V * w0.logits.element_size()
     variants["one_phase_every_row"]["row_pass_us"] = tv[0] * 1e3

@@ -205,6 +205,57 @@ rs_status rs_verify_greedy(const void* target_logits, rs_dtype logits_dtype,
                            int32_t* output_token_ids, int32_t* num_accepted, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
+/* ---- Tree verify --------------------------------------------------------
+ * The drafts of a request form a tree: node i holds one draft token and its
+ * parent (a node earlier in the request's node order, or -1 for a child of
+ * the last prefix position).  One target forward over the whole tree scored
+ * the prefix position and every node [投机解码深度实战 §四 (tree drafts and
+ * tree attention)].  Verification walks the tree one depth at a time from the
+ * root: among the current node's children it looks for an accepted one,
+ * descends into it, and stops at the first depth where none is accepted; one
+ * extra token then comes from the stop node's row
+ * [投机解码（Speculative Decoding）端到端深挖 §6.2].
+ *   greedy (T <= 0): the first child whose token is the row's argmax (lowest
+ *     index on argmax ties); else emit the argmax [§7.1].
+ *   random: p = softmax(row / T); one coin u_d per depth d (the accept uniform
+ *     of position d, see above); children in node order, a child repeating an
+ *     earlier sibling's token skipped; child i is accepted iff u_d < the sum
+ *     of p over the siblings up to and including i [§7.2, both thresholds at
+ *     their default 1]; if none, the extra token is the race over p without
+ *     the children's tokens (exponentials of depth d); a childless stop node
+ *     races over p (the bonus).
+ * Every sibling is accepted with probability p(its token) and the residual is
+ * p without the siblings, so each emitted token follows p; a tree with one
+ * child per node is exactly the chain of rs_verify with draft_probs = NULL
+ * (same tokens for the same seed).  Trees carry no draft probabilities.
+ * Layout:
+ *   cu_num_nodes  [B+1] int32: request b owns nodes cu[b] .. cu[b+1]-1
+ *   target_logits [N + B, V] fp32 / bf16: request b's rows start at
+ *                 cu[b] + b; row 0 is the prefix position (it predicts the
+ *                 children of the root), row 1 + i is node i
+ *   node_tokens   [N] int32 in [0, V); node_parents [N] int32, request-local,
+ *                 -1 <= parent < node
+ *   temperature   [B] fp32
+ *   output_token_ids [B, max_depth + 1] int32: the accepted path's tokens,
+ *                 then the extra token, then -1
+ *   accepted_nodes   [B, max_depth] int32: request-local indices of the
+ *                 accepted nodes, then -1
+ *   num_accepted     [B] int32: accepted nodes (path length)
+ * max_nodes <= RS_MAX_TREE_NODES bounds the nodes per request and max_depth
+ * <= max_nodes the depth (a node with no parent has depth 0); a request whose
+ * tree breaks these rules (too many nodes, a parent after its child, a token
+ * out of range, a node of depth >= max_depth) gets -1 rows and
+ * num_accepted = -1.  V <= RS_TREE_MAX_VOCAB.  One workgroup per request
+ * streams only the rows on its accepted path and the stop row; no workspace.
+ * Ownership, asynchrony and error reporting as for rs_verify. */
+#define RS_MAX_TREE_NODES 64
+#define RS_TREE_MAX_VOCAB 524288
+rs_status rs_verify_tree(const void* target_logits, rs_dtype logits_dtype, const int32_t* node_tokens,
+                         const int32_t* node_parents, const int32_t* cu_num_nodes, const float* temperature,
+                         int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_depth,
+                         int32_t vocab, uint64_t seed, int32_t* output_token_ids,
+                         int32_t* accepted_nodes, int32_t* num_accepted, hipStream_t stream);
+
 /* ---- Acceptance statistics ------------------------------------------------
  * Running counters a serving engine exports per verify step: draft proposals
  * (requests that proposed at least one draft -- proposals, not tokens),

@@ -19,11 +19,13 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 __all__ = ["verify", "verify_greedy", "workspace_size", "Debug", "RsVerifyError", "load_library",
-           "accept_stats_accumulate", "accept_rate", "accept_length", "MAX_SPEC_LEN", "STATS_COUNTERS",
+           "accept_stats_accumulate", "accept_rate", "accept_length", "verify_tree", "MAX_SPEC_LEN",
+           "MAX_TREE_NODES", "STATS_COUNTERS",
            "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librs_verify.so")
 MAX_SPEC_LEN = 32
+MAX_TREE_NODES = 64
 STATS_SCALARS = 5
 STATS_COUNTERS = STATS_SCALARS + MAX_SPEC_LEN
 
@@ -75,6 +77,8 @@ def load_library(path: str = LIB_PATH):
     lib.rs_verify_filtered.restype = ctypes.c_int
     lib.rs_verify_greedy.argtypes = [P, ctypes.c_int, P, P, i32, i32, i32, i32, P, P, P, sz, P]
     lib.rs_verify_greedy.restype = ctypes.c_int
+    lib.rs_verify_tree.argtypes = [P, ctypes.c_int, P, P, P, P, i32, i32, i32, i32, i32, u64, P, P, P, P]
+    lib.rs_verify_tree.restype = ctypes.c_int
     lib.rs_accept_stats_accumulate.argtypes = [P, P, i32, P, P]
     lib.rs_accept_stats_accumulate.restype = ctypes.c_int
     lib.rs_accept_rate.argtypes = [P]
@@ -304,3 +308,49 @@ def accept_length(counters) -> float:
     """tau = emitted tokens / verifies (rs_accept_length on a host copy)."""
     c = _host_counters(counters)
     return float(load_library().rs_accept_length(c.data_ptr()))
+
+
+def verify_tree(target_logits: torch.Tensor, node_tokens: torch.Tensor, node_parents: torch.Tensor,
+                cu_num_nodes: torch.Tensor, temperature: torch.Tensor, *, seed: int, max_nodes: int, max_depth: int,
+                out: Optional[torch.Tensor] = None, accepted_nodes: Optional[torch.Tensor] = None,
+                num_accepted: Optional[torch.Tensor] = None,
+                stream: Optional[torch.cuda.Stream] = None):
+    """Tree verify (rs_verify_tree).  Returns (output_token_ids [B, max_depth+1],
+    accepted_nodes [B, max_depth], num_accepted [B])."""
+    lib = load_library()
+    if not isinstance(target_logits, torch.Tensor) or target_logits.device.type != "cuda":
+        raise ValueError("target_logits must be a CUDA (HIP) tensor")
+    dev = target_logits.device
+    if target_logits.dtype not in _DTYPE:
+        raise TypeError(f"target_logits must be float32 or bfloat16, got {target_logits.dtype}")
+    _dev_tensor(target_logits, "target_logits", None, dev)
+    for t, name in ((node_tokens, "node_tokens"), (node_parents, "node_parents"), (cu_num_nodes, "cu_num_nodes")):
+        _dev_tensor(t, name, torch.int32, dev)
+    _dev_tensor(temperature, "temperature", torch.float32, dev)
+    V = int(target_logits.shape[-1])
+    B = int(cu_num_nodes.numel()) - 1
+    N = int(node_tokens.numel())
+    if B < 0 or node_parents.numel() != N or temperature.numel() != B:
+        raise ValueError("node_parents needs N entries, temperature B, cu_num_nodes B + 1")
+    if target_logits.numel() != (N + B) * V:
+        raise ValueError(f"target_logits must hold N + B = {N + B} rows")
+    if out is None:
+        out = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
+    if accepted_nodes is None:
+        accepted_nodes = torch.empty((B, max_depth), dtype=torch.int32, device=dev)
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    for t, name, n in ((out, "out", B * (max_depth + 1)), (accepted_nodes, "accepted_nodes", B * max_depth),
+                       (num_accepted, "num_accepted", B)):
+        _dev_tensor(t, name, torch.int32, dev)
+        if t.numel() != n:
+            raise ValueError(f"{name} must hold {n} int32 values")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    _check(lib.rs_verify_tree(
+        target_logits.data_ptr(), _DTYPE[target_logits.dtype], node_tokens.data_ptr() if N > 0 else None,
+        node_parents.data_ptr() if N > 0 else None, cu_num_nodes.data_ptr(), temperature.data_ptr(), B, N,
+        int(max_nodes), int(max_depth), V, int(seed) & ((1 << 64) - 1), out.data_ptr(),
+        accepted_nodes.data_ptr() if max_depth > 0 else None, num_accepted.data_ptr(),
+        ctypes.c_void_p(stream.cuda_stream)))
+    return out, accepted_nodes, num_accepted

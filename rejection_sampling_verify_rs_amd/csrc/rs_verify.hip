@@ -39,6 +39,7 @@
 #include "scan.hpp"
 #include "stats.hpp"
 #include "stream_path.hpp"
+#include "tree.hpp"
 
 namespace rsv {
 
@@ -592,6 +593,47 @@ rs_status rs_verify_greedy(const void* target_logits, rs_dtype logits_dtype, con
   return rsv::verify_impl(target_logits, logits_dtype, nullptr, draft_token_ids, cu_num_draft_tokens, nullptr,
                           nullptr, nullptr, 1, batch, total_draft_tokens, max_k, vocab, 0, output_token_ids,
                           num_accepted, workspace, workspace_bytes, nullptr, stream);
+}
+
+rs_status rs_verify_tree(const void* target_logits, rs_dtype logits_dtype, const int32_t* node_tokens,
+                         const int32_t* node_parents, const int32_t* cu_num_nodes, const float* temperature,
+                         int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_depth, int32_t vocab,
+                         uint64_t seed, int32_t* output_token_ids, int32_t* accepted_nodes, int32_t* num_accepted,
+                         hipStream_t stream) {
+  // Every check below runs before the launch.
+  if (batch < 0 || total_nodes < 0 || vocab < 1 || max_nodes < 0 || max_depth < 0) return RS_ERR_INVALID_ARG;
+  if (logits_dtype != RS_F32 && logits_dtype != RS_BF16) return RS_ERR_UNSUPPORTED;
+  if (batch == 0) return RS_OK;
+  if (max_nodes > RS_MAX_TREE_NODES || max_depth > max_nodes || (int64_t)total_nodes > (int64_t)batch * max_nodes)
+    return RS_ERR_INVALID_ARG;
+  if (vocab > RS_TREE_MAX_VOCAB) return RS_ERR_UNSUPPORTED;
+  if (!target_logits || !cu_num_nodes || !temperature || !output_token_ids || !num_accepted ||
+      (max_depth > 0 && !accepted_nodes) || (total_nodes > 0 && (!node_tokens || !node_parents)))
+    return RS_ERR_INVALID_ARG;
+  const size_t es = logits_dtype == RS_BF16 ? 2 : 4;
+  if (((uintptr_t)target_logits % es) || ((uintptr_t)node_tokens % 4) || ((uintptr_t)node_parents % 4) ||
+      ((uintptr_t)cu_num_nodes % 4) || ((uintptr_t)temperature % 4) || ((uintptr_t)output_token_ids % 4) ||
+      ((uintptr_t)accepted_nodes % 4) || ((uintptr_t)num_accepted % 4))
+    return RS_ERR_UNSUPPORTED;
+  const size_t lds = (size_t)((vocab + 31) / 32) * sizeof(uint32_t);
+  const bool big = vocab >= 65536;
+#define RS_TREE(ELEM, NT)                                                                                          \
+  rsv::tree_kernel<ELEM, NT><<<(unsigned)batch, NT, lds, stream>>>(                                               \
+      static_cast<const ELEM*>(target_logits), node_tokens, node_parents, cu_num_nodes, temperature, total_nodes, \
+      max_nodes, max_depth, vocab, seed, output_token_ids, accepted_nodes, num_accepted)
+  if (logits_dtype == RS_BF16) {
+    if (big)
+      RS_TREE(uint16_t, 1024);
+    else
+      RS_TREE(uint16_t, 256);
+  } else {
+    if (big)
+      RS_TREE(float, 1024);
+    else
+      RS_TREE(float, 256);
+  }
+#undef RS_TREE
+  return hipGetLastError() == hipSuccess ? RS_OK : RS_ERR_HIP;
 }
 
 rs_status rs_accept_stats_accumulate(const int32_t* num_accepted, const int32_t* cu_num_draft_tokens, int32_t batch,

@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
     assert _declared_functions() == ["rs_abi_version", "rs_accept_length", "rs_accept_rate",
                                      "rs_accept_stats_accumulate", "rs_status_string", "rs_verify",
                                      "rs_verify_filtered", "rs_verify_filtered_workspace_size", "rs_verify_greedy",
-                                     "rs_verify_workspace_size"]
+                                     "rs_verify_tree", "rs_verify_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -219,3 +219,35 @@ def test_stats_host_helpers(lib):
     import math
     assert math.isnan(lib.rs_accept_rate(np.zeros(rs.STATS_COUNTERS, np.int64).ctypes.data_as(ctypes.c_void_p)))
     assert math.isnan(lib.rs_accept_length(None))
+
+
+def _call_tree(lib, **kw):
+    a = dict(logits=DUMMY, dtype=1, tok=DUMMY, par=DUMMY, cu=DUMMY, T=DUMMY, B=2, N=10, max_nodes=8, max_depth=4,
+             V=100, seed=0, out=DUMMY, path=DUMMY, nacc=DUMMY, stream=None)
+    a.update(kw)
+    return lib.rs_verify_tree(a["logits"], a["dtype"], a["tok"], a["par"], a["cu"], a["T"], a["B"], a["N"],
+                              a["max_nodes"], a["max_depth"], a["V"], a["seed"], a["out"], a["path"], a["nacc"],
+                              a["stream"])
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), rs.RS_ERR_INVALID_ARG),
+    (dict(max_nodes=65, max_depth=4), rs.RS_ERR_INVALID_ARG),   # RS_MAX_TREE_NODES = 64
+    (dict(max_depth=9), rs.RS_ERR_INVALID_ARG),                 # deeper than max_nodes
+    (dict(N=17), rs.RS_ERR_INVALID_ARG),                        # N > B * max_nodes
+    (dict(V=524289), rs.RS_ERR_UNSUPPORTED),
+    (dict(dtype=3), rs.RS_ERR_UNSUPPORTED),
+    (dict(tok=None), rs.RS_ERR_INVALID_ARG),
+    (dict(path=None), rs.RS_ERR_INVALID_ARG),
+    (dict(T=None), rs.RS_ERR_INVALID_ARG),
+    (dict(logits=DUMMY + 1), rs.RS_ERR_UNSUPPORTED),
+    (dict(par=DUMMY + 2), rs.RS_ERR_UNSUPPORTED),
+])
+def test_tree_entry_validation(lib, kw, status):
+    assert _call_tree(lib, **kw) == status
+
+
+@needs_no_gpu
+def test_tree_entry_empty_batch(lib):
+    assert _call_tree(lib, B=0, N=0, logits=None, out=None, nacc=None) == rs.RS_OK

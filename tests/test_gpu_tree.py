@@ -1,0 +1,123 @@
+"""GPU parity of tree verify (rs_verify_tree through the C ABI) against the
+CPU oracle [投机解码深度实战 §四; 投机解码（Speculative Decoding）端到端深挖 §6.2,
+§7.1, §7.2]: accepted paths, counts and emitted tokens bit-exact on every
+request the oracle does not flag as a near tie; a one-child-per-node tree
+must give exactly the chain verify's output (rs_verify, no draft
+probabilities) on the GPU; invalid trees get -1 rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rejection_sampling_verify_rs_amd as rs
+import rs_workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device (run the CPU suite with -m 'not gpu')")
+    rs.load_library()
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def _run(w):
+    out, path, n = rs.verify_tree(w.logits, w.node_tokens, w.node_parents, w.cu_num_nodes, w.temperature,
+                                  seed=w.seed, max_nodes=w.max_nodes, max_depth=w.max_depth)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), path.cpu().numpy(), n.cpu().numpy()
+
+
+def _oracle(w):
+    c = w.to("cpu")
+    return oracle.verify_tree(c.logits, c.node_tokens, c.node_parents, c.cu_num_nodes, c.temperature, c.seed,
+                              c.max_nodes, c.max_depth)
+
+
+def _compare(w, g, o, max_flagged=1):
+    out, path, n = g
+    ok = ~o.near_tie
+    bad = np.nonzero(ok & ((n != o.num_accepted) | (out != o.tokens).any(1) | (path != o.path).any(1)))[0]
+    if bad.size:
+        b = int(bad[0])
+        raise AssertionError(f"{bad.size} unflagged requests differ; b={b}: gpu n={n[b]} out={out[b].tolist()} "
+                             f"path={path[b].tolist()} oracle n={o.num_accepted[b]} out={o.tokens[b].tolist()} "
+                             f"path={o.path[b].tolist()} flags={o.flags[b]}")
+    assert o.near_tie.sum() <= max_flagged
+    return int(o.near_tie.sum())
+
+
+CASES = [
+    # name, B, V, dtype, depth, branching, max_nodes, temperature
+    ("eagle bf16 V=151936 B=64", 64, 151936, torch.bfloat16, 5, (4, 2, 2, 1, 1), 64, ("uniform", 0.5, 1.2)),
+    ("eagle bf16 greedy V=151936", 32, 151936, torch.bfloat16, 5, (4, 2, 2, 1, 1), 64, 0.0),
+    ("wide fp32 V=32000 mixed", 40, 32000, torch.float32, 3, (8, 3, 1), 64, [0.0, 0.8, 1.0, -1.0] * 10),
+    ("deep bf16 V=50000", 24, 50000, torch.bfloat16, 8, (2, 2, 2, 1, 1, 1, 1, 1), 48, 1.0),
+    ("tiny V=7 fp32", 50, 7, torch.float32, 3, (3, 2, 1), 20, 0.9),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_tree_parity(case):
+    name, B, V, dt, depth, br, mn, T = case
+    w = W.make_tree(B, V, depth=depth, branching=br, max_nodes=mn, dtype=dt, temperature=T, seed=31,
+                    gen_seed=3000 + B, device="cuda", name=name)
+    _say(f"{name}: B={w.B} nodes/request={w.max_nodes} depth={w.max_depth}")
+    g = _run(w)
+    o = _oracle(w)
+    f = _compare(w, g, o)
+    _say(f"{name}: flagged {f}, mean accepted {o.num_accepted.mean():.3f}")
+
+
+def test_chain_tree_equals_chain_verify():
+    w = W.make([4, 0, 6, 3, 8, 1, 5, 2] * 8, 151936, dtype=torch.bfloat16, logit_std=3.0,
+               temperature=[0.7, 1.0, 0.0, 1.2] * 16, q_mode="none", draft_mode="argmax_mix", seed=9, gen_seed=91,
+               device="cuda")
+    parents = torch.tensor(np.concatenate([np.arange(k) - 1 for k in w.num_draft]).astype(np.int32), device="cuda")
+    out_c, n_c = rs.verify(w.logits, None, w.draft_token_ids, w.cu_num_draft_tokens, w.temperature, seed=w.seed,
+                           max_k=w.max_k)
+    out_t, path_t, n_t = rs.verify_tree(w.logits, w.draft_token_ids, parents, w.cu_num_draft_tokens, w.temperature,
+                                        seed=w.seed, max_nodes=w.max_k, max_depth=w.max_k)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(n_t.cpu().numpy(), n_c.cpu().numpy())
+    np.testing.assert_array_equal(out_t.cpu().numpy(), out_c.cpu().numpy())
+
+
+def test_duplicate_siblings_root_only_and_invalid():
+    V = 1000
+    g = torch.Generator().manual_seed(4)
+    # request 0: duplicate sibling tokens; 1: no nodes (bonus only); 2: parent after child (invalid);
+    # 3: token out of range (invalid); 4: a full 64-node star
+    trees = [([5, 5, 9, 5], [-1, -1, -1, 0]), ([], []), ([1, 2], [1, -1]), ([3, V + 2], [-1, 0]),
+             (list(range(100, 164)), [-1] * 64)]
+    tok = torch.tensor([t for tr in trees for t in tr[0]], dtype=torch.int32)
+    par = torch.tensor([p for tr in trees for p in tr[1]], dtype=torch.int32)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum([len(t[0]) for t in trees])]), dtype=torch.int32)
+    B, N = len(trees), int(cu[-1])
+    logits = torch.randn(N + B, V, generator=g) * 2
+    logits[:, 5] += 4  # make the duplicated token likely
+    T = torch.tensor([1.0, 0.8, 1.0, 1.0, 1.1])
+    w = W.TreeWorkload("edge", logits.cuda(), tok.cuda(), par.cuda(), cu.cuda(), T.cuda(), 17,
+                       [len(t[0]) for t in trees], 2)
+    w.num_nodes = [len(t[0]) for t in trees]
+    out, path, n = rs.verify_tree(w.logits, w.node_tokens, w.node_parents, w.cu_num_nodes, w.temperature, seed=17,
+                                  max_nodes=64, max_depth=2)
+    torch.cuda.synchronize()
+    o = oracle.verify_tree(logits, tok, par, cu, T, 17, 64, 2)
+    np.testing.assert_array_equal(n.cpu().numpy(), o.num_accepted)
+    np.testing.assert_array_equal(out.cpu().numpy(), o.tokens)
+    np.testing.assert_array_equal(path.cpu().numpy(), o.path)
+    assert o.num_accepted[2] == -1 and o.num_accepted[3] == -1
+
+
+def test_tree_rerun_bit_identical():
+    w = W.make_tree(32, 151936, temperature=1.0, seed=3, gen_seed=44, device="cuda")
+    a, b = _run(w), _run(w)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)

@@ -402,6 +402,22 @@ def main():
         f"{tw.N / (tms / 1e3):.3g} nodes/s, {np.mean(rows_read):.0f} of {tw.N + tw.B} rows streamed, "
         f"{dense / (tms / 1e3) / 1e9:.0f} GB/s effective (every row once)")
     del trees
+    # n-gram proposer (rs_ngram_propose): B=64 contexts of 4096 tokens,
+    # min_n 3, max_n 8, k 5 (the pages' example settings)
+    ctx, ccu = W.make_contexts(64, 4096, w0.V, seed=3, device=dev)
+    for _ in range(args.warmup):
+        rs.ngram_propose(ctx, ccu, min_n=3, max_n=8, k=5, stream=stream)
+    torch.cuda.synchronize()
+    s0.record(stream)
+    for _ in range(args.steps):
+        _, nprop, _ = rs.ngram_propose(ctx, ccu, min_n=3, max_n=8, k=5, stream=stream)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    nms = s0.elapsed_time(s1) / args.steps
+    variants["ngram_B64_ctx4096"] = {"us_per_step": nms * 1e3, "context_tokens_per_s": ctx.numel() / (nms / 1e3),
+                                     "mean_drafts": float(nprop.float().mean())}
+    log(f"ngram (B=64, 4096-token contexts): {nms * 1e3:.1f} us/step, {ctx.numel() / (nms / 1e3):.3g} context "
+        f"tokens/s, {float(nprop.float().mean()):.2f} drafts/request")
     tv = kernel_times(sampling_path=2, phase_ends=(-1,))
     lg = (w0.D + w0.B) * w0.V * w0.logits.element_size()
     variants["one_phase_every_row"]["row_pass_us"] = tv[0] * 1e3

@@ -256,6 +256,32 @@ rs_status rs_verify_tree(const void* target_logits, rs_dtype logits_dtype, const
                          int32_t vocab, uint64_t seed, int32_t* output_token_ids,
                          int32_t* accepted_nodes, int32_t* num_accepted, hipStream_t stream);
 
+/* ---- n-gram draft proposer -------------------------------------------------
+ * Prompt-lookup drafts for a batch of requests, ready for rs_verify with
+ * draft_probs = NULL [第12章 §12.4.4]: for n = max_n down to min_n, the
+ * pattern is the context's last n tokens; the proposal is the tokens after
+ * the leftmost earlier occurrence of the pattern (one ending before the
+ * pattern begins), at most k_b = min(k, max_model_len - len(context_b)) of
+ * them (fewer when the context ends first); the first n that matches wins;
+ * no match (or k_b <= 0) proposes nothing.
+ *   context_token_ids [total_context_tokens] int32 device, request b's tokens
+ *                     at cu_context[b] .. cu_context[b+1]-1 (cu_context [B+1])
+ *   1 <= min_n <= max_n <= RS_NGRAM_MAX_N, 1 <= k <= RS_MAX_SPEC_LEN
+ *   draft_token_ids     [B * k] int32 device: the proposals packed in request
+ *                       order (the first cu_num_draft_tokens[B] entries)
+ *   num_draft_tokens    [B] int32 device: proposals per request
+ *   cu_num_draft_tokens [B+1] int32 device: their prefix sums, from 0
+ *   workspace           >= B * k * 4 bytes of device scratch, 4-byte aligned
+ * A request whose context range is out of [0, total] proposes nothing.
+ * Errors and ownership as for rs_verify (RS_ERR_WORKSPACE for a missing or
+ * short workspace). */
+#define RS_NGRAM_MAX_N 64
+rs_status rs_ngram_propose(const int32_t* context_token_ids, const int32_t* cu_context, int32_t batch,
+                           int32_t total_context_tokens, int32_t min_n, int32_t max_n, int32_t k,
+                           int64_t max_model_len, int32_t* draft_token_ids, int32_t* num_draft_tokens,
+                           int32_t* cu_num_draft_tokens, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
 /* ---- Acceptance statistics ------------------------------------------------
  * Running counters a serving engine exports per verify step: draft proposals
  * (requests that proposed at least one draft -- proposals, not tokens),

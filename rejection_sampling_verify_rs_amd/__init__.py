@@ -20,7 +20,7 @@ import torch
 
 __all__ = ["verify", "verify_greedy", "workspace_size", "Debug", "RsVerifyError", "load_library",
            "accept_stats_accumulate", "accept_rate", "accept_length", "verify_tree", "MAX_SPEC_LEN",
-           "MAX_TREE_NODES", "STATS_COUNTERS",
+           "MAX_TREE_NODES", "STATS_COUNTERS", "ngram_propose",
            "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librs_verify.so")
@@ -79,6 +79,8 @@ def load_library(path: str = LIB_PATH):
     lib.rs_verify_greedy.restype = ctypes.c_int
     lib.rs_verify_tree.argtypes = [P, ctypes.c_int, P, P, P, P, i32, i32, i32, i32, i32, u64, P, P, P, P]
     lib.rs_verify_tree.restype = ctypes.c_int
+    lib.rs_ngram_propose.argtypes = [P, P, i32, i32, i32, i32, i32, ctypes.c_int64, P, P, P, P, sz, P]
+    lib.rs_ngram_propose.restype = ctypes.c_int
     lib.rs_accept_stats_accumulate.argtypes = [P, P, i32, P, P]
     lib.rs_accept_stats_accumulate.restype = ctypes.c_int
     lib.rs_accept_rate.argtypes = [P]
@@ -354,3 +356,31 @@ def verify_tree(target_logits: torch.Tensor, node_tokens: torch.Tensor, node_par
         accepted_nodes.data_ptr() if max_depth > 0 else None, num_accepted.data_ptr(),
         ctypes.c_void_p(stream.cuda_stream)))
     return out, accepted_nodes, num_accepted
+
+
+def ngram_propose(context_token_ids: torch.Tensor, cu_context: torch.Tensor, *, min_n: int, max_n: int, k: int,
+                  max_model_len: int = 1 << 62, stream: Optional[torch.cuda.Stream] = None):
+    """n-gram drafts (rs_ngram_propose).  Returns (draft_token_ids packed [B * k],
+    num_draft_tokens [B], cu_num_draft_tokens [B + 1]); the first
+    cu_num_draft_tokens[-1] drafts are valid."""
+    lib = load_library()
+    if not isinstance(context_token_ids, torch.Tensor) or context_token_ids.device.type != "cuda":
+        raise ValueError("context_token_ids must be a CUDA (HIP) tensor")
+    dev = context_token_ids.device
+    _dev_tensor(context_token_ids, "context_token_ids", torch.int32, dev)
+    _dev_tensor(cu_context, "cu_context", torch.int32, dev)
+    B = int(cu_context.numel()) - 1
+    if B < 0:
+        raise ValueError("cu_context needs B + 1 entries")
+    drafts = torch.empty(max(B * k, 1), dtype=torch.int32, device=dev)
+    num = torch.empty(max(B, 1), dtype=torch.int32, device=dev)[:B]
+    cu = torch.zeros(B + 1, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(B * k, 1), dtype=torch.int32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    T = int(context_token_ids.numel())
+    _check(lib.rs_ngram_propose(context_token_ids.data_ptr() if T > 0 else None, cu_context.data_ptr(), B, T,
+                                int(min_n), int(max_n), int(k), int(max_model_len), drafts.data_ptr(),
+                                num.data_ptr() if B > 0 else None, cu.data_ptr(), ws.data_ptr(),
+                                ws.numel() * 4, ctypes.c_void_p(stream.cuda_stream)))
+    return drafts[: B * k], num, cu

@@ -37,6 +37,7 @@
 #include "row_pass.hpp"
 #include "rs_verify.h"
 #include "scan.hpp"
+#include "ngram.hpp"
 #include "stats.hpp"
 #include "stream_path.hpp"
 #include "tree.hpp"
@@ -633,6 +634,32 @@ rs_status rs_verify_tree(const void* target_logits, rs_dtype logits_dtype, const
       RS_TREE(float, 256);
   }
 #undef RS_TREE
+  return hipGetLastError() == hipSuccess ? RS_OK : RS_ERR_HIP;
+}
+
+rs_status rs_ngram_propose(const int32_t* context_token_ids, const int32_t* cu_context, int32_t batch,
+                           int32_t total_context_tokens, int32_t min_n, int32_t max_n, int32_t k,
+                           int64_t max_model_len, int32_t* draft_token_ids, int32_t* num_draft_tokens,
+                           int32_t* cu_num_draft_tokens, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  // Every check below runs before the first launch.
+  if (batch < 0 || total_context_tokens < 0) return RS_ERR_INVALID_ARG;
+  if (min_n < 1 || max_n < min_n || max_n > RS_NGRAM_MAX_N || k < 1 || k > RS_MAX_SPEC_LEN) return RS_ERR_INVALID_ARG;
+  if (batch == 0) return RS_OK;
+  if (!cu_context || !draft_token_ids || !num_draft_tokens || !cu_num_draft_tokens ||
+      (total_context_tokens > 0 && !context_token_ids))
+    return RS_ERR_INVALID_ARG;
+  if (((uintptr_t)context_token_ids % 4) || ((uintptr_t)cu_context % 4) || ((uintptr_t)draft_token_ids % 4) ||
+      ((uintptr_t)num_draft_tokens % 4) || ((uintptr_t)cu_num_draft_tokens % 4))
+    return RS_ERR_UNSUPPORTED;
+  if (!workspace || ((uintptr_t)workspace % 4) || workspace_bytes < (size_t)batch * k * sizeof(int32_t))
+    return RS_ERR_WORKSPACE;
+  int32_t* padded = static_cast<int32_t*>(workspace);
+  rsv::ngram_kernel<<<(unsigned)batch, rsv::kNgramThreads, 0, stream>>>(
+      context_token_ids, cu_context, total_context_tokens, min_n, max_n, k, max_model_len, padded, num_draft_tokens);
+  if (hipGetLastError() != hipSuccess) return RS_ERR_HIP;
+  rsv::ngram_pack_kernel<<<1, 1024, 0, stream>>>(padded, num_draft_tokens, batch, k, draft_token_ids,
+                                                 cu_num_draft_tokens);
   return hipGetLastError() == hipSuccess ? RS_OK : RS_ERR_HIP;
 }
 

@@ -333,3 +333,33 @@ def make_tree(B: int, V: int, *, depth: int = 5, branching=(4, 2, 2, 1, 1), max_
         depth_of.append(0 if p_ < 0 else depth_of[p_] + 1)
     return TreeWorkload(name, logits.contiguous(), tokens.reshape(-1).to(device), par.repeat(B).to(device),
                         cu.to(device), T.contiguous(), int(seed), [n] * B, (max(depth_of) + 1) if depth_of else 0)
+
+
+def make_contexts(B: int, length, vocab: int = 151936, *, copy_prob: float = 0.5, span=(8, 48), seed: int = 0,
+                  device="cpu"):
+    """Token contexts with repetition, the setting the n-gram proposer targets
+    (code, templated text): each context is built span by span; with
+    probability copy_prob a span copies an earlier stretch of the same context,
+    else it is fresh tokens drawn from a Zipf-like law over the vocabulary.
+    length is an int or a (lo, hi) range per request.  Returns (flat int32
+    tokens, cu [B + 1] int32)."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    ranks = np.arange(1, vocab + 1, dtype=np.float64)
+    pz = 1.0 / ranks ** 1.1
+    pz /= pz.sum()
+    ctxs = []
+    for b in range(B):
+        L = int(length) if np.isscalar(length) else int(rng.integers(length[0], length[1] + 1))
+        c = []
+        while len(c) < L:
+            n = int(rng.integers(span[0], span[1] + 1))
+            if c and len(c) > span[0] and rng.random() < copy_prob:
+                st = int(rng.integers(0, len(c) - 1))
+                c.extend(c[st:st + n])
+            else:
+                c.extend(rng.choice(vocab, size=n, p=pz).tolist())
+        ctxs.append(c[:L])
+    flat = torch.tensor([t for c in ctxs for t in c], dtype=torch.int32, device=device)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum([len(c) for c in ctxs])]), dtype=torch.int32, device=device)
+    return flat, cu

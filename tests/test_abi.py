@@ -28,7 +28,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert _declared_functions() == ["rs_abi_version", "rs_accept_length", "rs_accept_rate",
-                                     "rs_accept_stats_accumulate", "rs_status_string", "rs_verify",
+                                     "rs_accept_stats_accumulate", "rs_ngram_propose", "rs_status_string",
+                                     "rs_verify",
                                      "rs_verify_filtered", "rs_verify_filtered_workspace_size", "rs_verify_greedy",
                                      "rs_verify_tree", "rs_verify_workspace_size"]
 
@@ -251,3 +252,26 @@ def test_tree_entry_validation(lib, kw, status):
 @needs_no_gpu
 def test_tree_entry_empty_batch(lib):
     assert _call_tree(lib, B=0, N=0, logits=None, out=None, nacc=None) == rs.RS_OK
+
+
+@needs_no_gpu
+def test_ngram_entry_validation(lib):
+    f = lib.rs_ngram_propose
+
+    def g(**kw):
+        a = dict(ctx=DUMMY, cu=DUMMY, B=2, T=100, mn=2, mx=4, k=5, mml=1 << 40, d=DUMMY, n=DUMMY, c=DUMMY, ws=DUMMY,
+                 wsb=1 << 20)
+        a.update(kw)
+        return f(a["ctx"], a["cu"], a["B"], a["T"], a["mn"], a["mx"], a["k"], a["mml"], a["d"], a["n"], a["c"],
+                 a["ws"], a["wsb"], None)
+
+    assert g(B=-1) == rs.RS_ERR_INVALID_ARG
+    assert g(mn=0) == rs.RS_ERR_INVALID_ARG
+    assert g(mx=1) == rs.RS_ERR_INVALID_ARG          # max_n < min_n
+    assert g(mx=65) == rs.RS_ERR_INVALID_ARG         # RS_NGRAM_MAX_N = 64
+    assert g(k=33) == rs.RS_ERR_INVALID_ARG          # RS_MAX_SPEC_LEN = 32
+    assert g(cu=None) == rs.RS_ERR_INVALID_ARG
+    assert g(ctx=DUMMY + 2) == rs.RS_ERR_UNSUPPORTED
+    assert g(wsb=2 * 5 * 4 - 1) == rs.RS_ERR_WORKSPACE
+    assert g(ws=None) == rs.RS_ERR_WORKSPACE
+    assert g(B=0, ctx=None, cu=None, d=None, n=None, c=None, ws=None) == rs.RS_OK

@@ -369,6 +369,7 @@ def main():
     trees = [W.make_tree(64, w0.V, temperature=("uniform", 0.5, 1.2), seed=7, gen_seed=5000 + i, device=dev)
              for i in range(args.copies)]
     tw = trees[0]
+    tws = torch.empty((rs.load_library().rs_verify_tree_workspace_size(tw.B, tw.V),), dtype=torch.uint8, device=dev)
     tout = torch.empty((tw.B, tw.max_depth + 1), dtype=torch.int32, device=dev)
     tpath = torch.empty((tw.B, tw.max_depth), dtype=torch.int32, device=dev)
     tn = torch.empty((tw.B,), dtype=torch.int32, device=dev)
@@ -377,7 +378,7 @@ def main():
         t = trees[i % args.copies]
         rs.verify_tree(t.logits, t.node_tokens, t.node_parents, t.cu_num_nodes, t.temperature, seed=t.seed,
                        max_nodes=t.max_nodes, max_depth=t.max_depth, out=tout, accepted_nodes=tpath,
-                       num_accepted=tn, stream=stream)
+                       num_accepted=tn, workspace=tws, stream=stream)
 
     for k in range(args.warmup):
         tree_call(k)

@@ -246,15 +246,21 @@ rs_status rs_verify_greedy(const void* target_logits, rs_dtype logits_dtype,
  * tree breaks these rules (too many nodes, a parent after its child, a token
  * out of range, a node of depth >= max_depth) gets -1 rows and
  * num_accepted = -1.  V <= RS_TREE_MAX_VOCAB.  One workgroup per request
- * streams only the rows on its accepted path and the stop row; no workspace.
+ * walks the tree, streaming only the rows on its accepted path and the stop
+ * row; the final race of random requests is spread over the GPU.
+ *   workspace  >= rs_verify_tree_workspace_size(B, V) bytes, 16-byte aligned
+ *              (RS_ERR_WORKSPACE otherwise); calls sharing one workspace must
+ *              not overlap.
  * Ownership, asynchrony and error reporting as for rs_verify. */
 #define RS_MAX_TREE_NODES 64
 #define RS_TREE_MAX_VOCAB 524288
+size_t rs_verify_tree_workspace_size(int32_t batch, int32_t vocab);
 rs_status rs_verify_tree(const void* target_logits, rs_dtype logits_dtype, const int32_t* node_tokens,
                          const int32_t* node_parents, const int32_t* cu_num_nodes, const float* temperature,
                          int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_depth,
                          int32_t vocab, uint64_t seed, int32_t* output_token_ids,
-                         int32_t* accepted_nodes, int32_t* num_accepted, hipStream_t stream);
+                         int32_t* accepted_nodes, int32_t* num_accepted, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
 
 /* ---- n-gram draft proposer -------------------------------------------------
  * Prompt-lookup drafts for a batch of requests, ready for rs_verify with

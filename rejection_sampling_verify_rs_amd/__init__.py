@@ -77,7 +77,9 @@ def load_library(path: str = LIB_PATH):
     lib.rs_verify_filtered.restype = ctypes.c_int
     lib.rs_verify_greedy.argtypes = [P, ctypes.c_int, P, P, i32, i32, i32, i32, P, P, P, sz, P]
     lib.rs_verify_greedy.restype = ctypes.c_int
-    lib.rs_verify_tree.argtypes = [P, ctypes.c_int, P, P, P, P, i32, i32, i32, i32, i32, u64, P, P, P, P]
+    lib.rs_verify_tree.argtypes = [P, ctypes.c_int, P, P, P, P, i32, i32, i32, i32, i32, u64, P, P, P, P, sz, P]
+    lib.rs_verify_tree_workspace_size.argtypes = [i32, i32]
+    lib.rs_verify_tree_workspace_size.restype = sz
     lib.rs_verify_tree.restype = ctypes.c_int
     lib.rs_ngram_propose.argtypes = [P, P, i32, i32, i32, i32, i32, ctypes.c_int64, P, P, P, P, sz, P]
     lib.rs_ngram_propose.restype = ctypes.c_int
@@ -315,7 +317,7 @@ def accept_length(counters) -> float:
 def verify_tree(target_logits: torch.Tensor, node_tokens: torch.Tensor, node_parents: torch.Tensor,
                 cu_num_nodes: torch.Tensor, temperature: torch.Tensor, *, seed: int, max_nodes: int, max_depth: int,
                 out: Optional[torch.Tensor] = None, accepted_nodes: Optional[torch.Tensor] = None,
-                num_accepted: Optional[torch.Tensor] = None,
+                num_accepted: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                 stream: Optional[torch.cuda.Stream] = None):
     """Tree verify (rs_verify_tree).  Returns (output_token_ids [B, max_depth+1],
     accepted_nodes [B, max_depth], num_accepted [B])."""
@@ -347,14 +349,18 @@ def verify_tree(target_logits: torch.Tensor, node_tokens: torch.Tensor, node_par
         _dev_tensor(t, name, torch.int32, dev)
         if t.numel() != n:
             raise ValueError(f"{name} must hold {n} int32 values")
+    if workspace is None:
+        workspace = torch.empty((max(int(lib.rs_verify_tree_workspace_size(B, V)), 1),), dtype=torch.uint8,
+                                device=dev)
+    _dev_tensor(workspace, "workspace", torch.uint8, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     _check(lib.rs_verify_tree(
         target_logits.data_ptr(), _DTYPE[target_logits.dtype], node_tokens.data_ptr() if N > 0 else None,
         node_parents.data_ptr() if N > 0 else None, cu_num_nodes.data_ptr(), temperature.data_ptr(), B, N,
         int(max_nodes), int(max_depth), V, int(seed) & ((1 << 64) - 1), out.data_ptr(),
-        accepted_nodes.data_ptr() if max_depth > 0 else None, num_accepted.data_ptr(),
-        ctypes.c_void_p(stream.cuda_stream)))
+        accepted_nodes.data_ptr() if max_depth > 0 else None, num_accepted.data_ptr(), workspace.data_ptr(),
+        workspace.numel(), ctypes.c_void_p(stream.cuda_stream)))
     return out, accepted_nodes, num_accepted
 
 

@@ -365,7 +365,7 @@ static bool launch_stream_kernels(StreamArgs<Elem>& a, hipStream_t stream, Event
   stream_kernel<Elem, NV, TPT><<<(unsigned)a.n_tasks, kRowThreads, 0, stream>>>(a);
   if (!evl.after_kernel(stream)) return false;
   if (a.n_race > 0) {
-    stream_race_tail_kernel<Elem, TPT><<<(unsigned)a.n_race, kRaceThreads, 0, stream>>>(a);
+    stream_race_tail_kernel<Elem, TPT><<<(unsigned)a.B, kRaceThreads, 0, stream>>>(a);
     if (!evl.after_kernel(stream)) return false;
   }
   return true;
@@ -596,12 +596,24 @@ rs_status rs_verify_greedy(const void* target_logits, rs_dtype logits_dtype, con
                           num_accepted, workspace, workspace_bytes, nullptr, stream);
 }
 
+static int32_t tree_chunks(int32_t vocab) {
+  constexpr int32_t kChunk = rsv::kRaceThreads * rsv::kTreeRaceTPT;
+  return (vocab + kChunk - 1) / kChunk;
+}
+
+size_t rs_verify_tree_workspace_size(int32_t batch, int32_t vocab) {
+  if (batch < 0 || vocab < 1) return 0;
+  if (batch == 0) return 0;
+  const size_t rec = ((size_t)batch * sizeof(rsv::ReqRecord) + 255) / 256 * 256;
+  return rec + (size_t)batch * tree_chunks(vocab) * sizeof(unsigned long long);
+}
+
 rs_status rs_verify_tree(const void* target_logits, rs_dtype logits_dtype, const int32_t* node_tokens,
                          const int32_t* node_parents, const int32_t* cu_num_nodes, const float* temperature,
                          int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_depth, int32_t vocab,
                          uint64_t seed, int32_t* output_token_ids, int32_t* accepted_nodes, int32_t* num_accepted,
-                         hipStream_t stream) {
-  // Every check below runs before the launch.
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  // Every check below runs before the first launch.
   if (batch < 0 || total_nodes < 0 || vocab < 1 || max_nodes < 0 || max_depth < 0) return RS_ERR_INVALID_ARG;
   if (logits_dtype != RS_F32 && logits_dtype != RS_BF16) return RS_ERR_UNSUPPORTED;
   if (batch == 0) return RS_OK;
@@ -616,24 +628,41 @@ rs_status rs_verify_tree(const void* target_logits, rs_dtype logits_dtype, const
       ((uintptr_t)cu_num_nodes % 4) || ((uintptr_t)temperature % 4) || ((uintptr_t)output_token_ids % 4) ||
       ((uintptr_t)accepted_nodes % 4) || ((uintptr_t)num_accepted % 4))
     return RS_ERR_UNSUPPORTED;
-  const size_t lds = (size_t)((vocab + 31) / 32) * sizeof(uint32_t);
+  if (!workspace || ((uintptr_t)workspace % 16) || workspace_bytes < rs_verify_tree_workspace_size(batch, vocab))
+    return RS_ERR_WORKSPACE;
+  rsv::ReqRecord* records = static_cast<rsv::ReqRecord*>(workspace);
+  unsigned long long* cand = reinterpret_cast<unsigned long long*>(
+      static_cast<char*>(workspace) + ((size_t)batch * sizeof(rsv::ReqRecord) + 255) / 256 * 256);
+  const int32_t nchunks = tree_chunks(vocab);
   const bool big = vocab >= 65536;
 #define RS_TREE(ELEM, NT)                                                                                          \
-  rsv::tree_kernel<ELEM, NT><<<(unsigned)batch, NT, lds, stream>>>(                                               \
+  rsv::tree_kernel<ELEM, NT><<<(unsigned)batch, NT, 0, stream>>>(                                                 \
       static_cast<const ELEM*>(target_logits), node_tokens, node_parents, cu_num_nodes, temperature, total_nodes, \
-      max_nodes, max_depth, vocab, seed, output_token_ids, accepted_nodes, num_accepted)
+      max_nodes, max_depth, vocab, seed, output_token_ids, accepted_nodes, num_accepted, records)
+#define RS_TREE_RACE(ELEM)                                                                                         \
+  rsv::tree_race_kernel<ELEM><<<(unsigned)((int64_t)batch * nchunks), rsv::kRaceThreads, 0, stream>>>(            \
+      static_cast<const ELEM*>(target_logits), node_tokens, node_parents, vocab, seed, nchunks, records, cand);    \
+  if (hipGetLastError() != hipSuccess) return RS_ERR_HIP;                                                          \
+  rsv::tree_emit_kernel<ELEM><<<(unsigned)batch, 64, 0, stream>>>(static_cast<const ELEM*>(target_logits),        \
+                                                                  max_depth, vocab, seed, nchunks, records, cand, \
+                                                                  output_token_ids, num_accepted)
   if (logits_dtype == RS_BF16) {
     if (big)
       RS_TREE(uint16_t, 1024);
     else
       RS_TREE(uint16_t, 256);
+    if (hipGetLastError() != hipSuccess) return RS_ERR_HIP;
+    RS_TREE_RACE(uint16_t);
   } else {
     if (big)
       RS_TREE(float, 1024);
     else
       RS_TREE(float, 256);
+    if (hipGetLastError() != hipSuccess) return RS_ERR_HIP;
+    RS_TREE_RACE(float);
   }
 #undef RS_TREE
+#undef RS_TREE_RACE
   return hipGetLastError() == hipSuccess ? RS_OK : RS_ERR_HIP;
 }
 

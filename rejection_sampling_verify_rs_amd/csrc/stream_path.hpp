@@ -29,7 +29,7 @@
 //     position, take the requests in the order they were decided, after a
 //     short bounded poll of an empty slot;
 //   * the tail kernel, launched when every request is decided, claims every
-//     chunk still unclaimed.
+//     chunk still unclaimed (one workgroup per queue slot, looping).
 // The last chunk of a request to be raced writes its output row.
 #pragma once
 
@@ -202,28 +202,30 @@ __device__ __forceinline__ void stream_row_complete(const StreamArgs<Elem>& a, i
 }
 
 // Claim and race one chunk of request b's race (whole workgroup); the last
-// chunk raced writes the output row.  Returns without work once every chunk is
-// claimed.
+// chunk raced writes the output row.  Returns false, without work, once every
+// chunk is claimed (the same answer in every thread).
 template <typename Elem, int TPT>
-__device__ __forceinline__ void stream_race_claim(const StreamArgs<Elem>& a, int32_t b, int32_t* s_word) {
+__device__ __forceinline__ bool stream_race_claim(const StreamArgs<Elem>& a, int32_t b, int32_t* s_word) {
   const int tid = threadIdx.x;
   uint32_t* ctl = a.race_ctl + (int64_t)b * kRaceCtlStride;
   if (tid == 0)
     *s_word = (int32_t)__hip_atomic_fetch_add(ctl + 16, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  const int32_t c = *s_word;
-  if (c >= a.race_chunks) return;
+  const int32_t c = *s_word;  // every thread reads it before race_chunk's barriers
+  if (c >= a.race_chunks) return false;
   const ReqRecord rec = load_record(a.records + b);
   const unsigned long long packed = race_chunk<Elem, TPT>(a.logits, a.q, a.V, a.seed, rec, b, c);
-  if (tid >= 64) return;  // wavefront 0 reports the chunk winner
-  int last = 0;
-  if (tid == 0) {
-    store_coherent(a.cand + (int64_t)b * a.race_chunks + c, packed);
-    wait_memory();
-    last = arrive_last(ctl, (uint32_t)a.race_chunks);
+  if (tid < 64) {  // wavefront 0 reports the chunk winner
+    int last = 0;
+    if (tid == 0) {
+      store_coherent(a.cand + (int64_t)b * a.race_chunks + c, packed);
+      wait_memory();
+      last = arrive_last(ctl, (uint32_t)a.race_chunks);
+    }
+    if (__shfl(last, 0))
+      finish_request<Elem>(a.logits, a.draft, a.max_k, a.V, a.race_chunks, a.seed, rec, b, a.cand, a.out, a.nacc);
   }
-  if (__shfl(last, 0))
-    finish_request<Elem>(a.logits, a.draft, a.max_k, a.V, a.race_chunks, a.seed, rec, b, a.cand, a.out, a.nacc);
+  return true;
 }
 
 // Chunk c of row j of request b, unless the request is invalid, has fewer
@@ -247,7 +249,7 @@ __device__ __forceinline__ void stream_row_task(const StreamArgs<Elem>& a, int32
   const int32_t K = e - s;  // in range: the init kernel validated the request
   if (j > K) return;
   if (st >= 2 && ((st - 2) & (kStateReady - 1)) < j) {  // decided before position j: row not needed
-    if (st >= kStateReady) stream_race_claim<Elem, TPT>(a, b, s_word);
+    if (st >= kStateReady) (void)stream_race_claim<Elem, TPT>(a, b, s_word);
     return;
   }
   const int32_t xstar = (c == 0 && j < K && T > 0.f) ? a.draft[s + j] : -1;
@@ -264,7 +266,8 @@ __device__ __forceinline__ void stream_row_task(const StreamArgs<Elem>& a, int32
 
 // Race task of queue slot `slot`: the request decided slot-th.  In the stream
 // kernel (tail == false) an empty slot is polled briefly and then left to the
-// tail kernel, where every slot is filled.
+// tail kernel, where every slot is filled and the workgroup races chunks of
+// its request until none is left to claim.
 template <typename Elem, int TPT>
 __device__ __forceinline__ void stream_race_task(const StreamArgs<Elem>& a, int32_t slot, bool tail,
                                                  int32_t* s_word) {
@@ -281,7 +284,12 @@ __device__ __forceinline__ void stream_race_task(const StreamArgs<Elem>& a, int3
   const int32_t v = *s_word;
   __syncthreads();  // s_word is reused below
   if (v == 0 || v == kQueueSkip) return;  // empty (left to the tail kernel) or nothing to race
-  stream_race_claim<Elem, TPT>(a, v - 1, s_word);
+  if (!tail) {
+    (void)stream_race_claim<Elem, TPT>(a, v - 1, s_word);
+    return;
+  }
+  while (stream_race_claim<Elem, TPT>(a, v - 1, s_word)) {
+  }
 }
 
 template <typename Elem, int NV, int TPT>
@@ -313,12 +321,12 @@ __global__ __launch_bounds__(kRowThreads) void stream_kernel(StreamArgs<Elem> a)
                                  (int32_t)(k % a.nsplit), &s_word);
 }
 
-// Every race chunk still unclaimed after the stream kernel (one workgroup per
-// (queue slot, chunk); each claims at most one chunk).
+// Every race chunk still unclaimed after the stream kernel: one workgroup per
+// queue slot races the chunks of its request that nobody claimed yet.
 template <typename Elem, int TPT>
 __global__ __launch_bounds__(kRaceThreads) void stream_race_tail_kernel(StreamArgs<Elem> a) {
   __shared__ int32_t s_word;
-  stream_race_task<Elem, TPT>(a, (int32_t)(blockIdx.x / a.race_chunks), true, &s_word);
+  stream_race_task<Elem, TPT>(a, (int32_t)blockIdx.x, true, &s_word);
 }
 
 // One wavefront per request: validity, counters, masks, state; -1 row for an

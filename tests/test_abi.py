@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
                                      "rs_accept_stats_accumulate", "rs_ngram_propose", "rs_status_string",
                                      "rs_verify",
                                      "rs_verify_filtered", "rs_verify_filtered_workspace_size", "rs_verify_greedy",
-                                     "rs_verify_tree", "rs_verify_workspace_size"]
+                                     "rs_verify_tree", "rs_verify_tree_workspace_size", "rs_verify_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -224,11 +224,11 @@ def test_stats_host_helpers(lib):
 
 def _call_tree(lib, **kw):
     a = dict(logits=DUMMY, dtype=1, tok=DUMMY, par=DUMMY, cu=DUMMY, T=DUMMY, B=2, N=10, max_nodes=8, max_depth=4,
-             V=100, seed=0, out=DUMMY, path=DUMMY, nacc=DUMMY, stream=None)
+             V=100, seed=0, out=DUMMY, path=DUMMY, nacc=DUMMY, ws=DUMMY, wsb=1 << 20, stream=None)
     a.update(kw)
     return lib.rs_verify_tree(a["logits"], a["dtype"], a["tok"], a["par"], a["cu"], a["T"], a["B"], a["N"],
                               a["max_nodes"], a["max_depth"], a["V"], a["seed"], a["out"], a["path"], a["nacc"],
-                              a["stream"])
+                              a["ws"], a["wsb"], a["stream"])
 
 
 @needs_no_gpu
@@ -244,6 +244,8 @@ def _call_tree(lib, **kw):
     (dict(T=None), rs.RS_ERR_INVALID_ARG),
     (dict(logits=DUMMY + 1), rs.RS_ERR_UNSUPPORTED),
     (dict(par=DUMMY + 2), rs.RS_ERR_UNSUPPORTED),
+    (dict(ws=None), rs.RS_ERR_WORKSPACE),
+    (dict(wsb=8), rs.RS_ERR_WORKSPACE),
 ])
 def test_tree_entry_validation(lib, kw, status):
     assert _call_tree(lib, **kw) == status

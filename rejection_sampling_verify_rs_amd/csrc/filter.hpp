@@ -39,8 +39,10 @@
 
 namespace rsv {
 
-constexpr int kFilterThreads = 256;
-constexpr int kFilterBins = 256;      // one radix digit of 8 bits: one bin per thread
+constexpr int kFilterThreads = 256;  // a workgroup per row
+constexpr int kFilterBins = 256;      // one radix digit of 8 bits: bin t owned by thread t of the first 256
+constexpr int kRankMax = 256;         // lists ranked directly (larger ones by radix selection)
+constexpr int kRankParts = kFilterThreads / kRankMax;  // threads sharing one value's ranking
 // Histogram copies, chosen by lane & 3, so fewer lanes of one wavefront
 // instruction add to the same LDS word (same-address atomics serialise); copy
 // c starts at c * kHistStride words so equal bins of different copies sit in
@@ -48,6 +50,7 @@ constexpr int kFilterBins = 256;      // one radix digit of 8 bits: one bin per 
 constexpr int kHistCopies = 4;
 constexpr int kHistStride = kFilterBins + 1;
 constexpr int kFilterCand = 4096;     // candidate list entries in LDS
+constexpr int kStashW = 1024;         // per-wavefront LDS queue of window elements (select_row)
 constexpr int kFilterSegList = 1024;  // segments re-read per row at most
 constexpr int kSegVectors = 16;       // 16-byte vectors per segment: the row task's vectors per thread
 
@@ -73,9 +76,13 @@ __device__ __forceinline__ bool filter_on(const int32_t* __restrict__ top_k, con
   return false;
 }
 
-// Order-preserving key: key(a) < key(b) iff a < b for non-NaN floats.
+// Order-preserving key: key(a) < key(b) iff a < b, and key(a) == key(b) iff
+// a == b, for non-NaN floats.  -0 and +0 are one value and get one key (that
+// of +0): the kept set is decided by comparing values, and the selections and
+// sums by comparing keys, so the two must agree on ties.
 __device__ __forceinline__ uint32_t order_key(float v) {
-  const uint32_t u = __float_as_uint(v);
+  uint32_t u = __float_as_uint(v);
+  u = u == 0x80000000u ? 0u : u;
   return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float key_value(uint32_t k) {
@@ -126,7 +133,7 @@ struct RowView {
 // the calling thread holds.
 template <typename Elem>
 struct RowVisitor {  // the whole row, read from memory kRowBatch vectors per thread at a time
-  static constexpr int kRowBatch = 16;
+  static constexpr int kRowBatch = 4096 / kFilterThreads;
   RowView<Elem> rv;
   template <typename F>
   __device__ __forceinline__ void operator()(F&& f) const {
@@ -147,8 +154,30 @@ struct RowVisitor {  // the whole row, read from memory kRowBatch vectors per th
     float e;
     if (threadIdx.x < 16 && rv.extra(threadIdx.x, e)) f(e);
   }
+  // The same elements, but f runs on every lane at every step (-inf where the
+  // lane holds no element), so that f may use wavefront-wide operations.
+  template <typename F>
+  __device__ __forceinline__ void uniform(F&& f) const {
+    using VT = Vec<Elem>;
+    for (int base = 0; base < rv.nvec; base += kRowBatch * kFilterThreads) {
+      const int v0 = base + (int)threadIdx.x;
+      uint4 x[kRowBatch];
+#pragma unroll
+      for (int i = 0; i < kRowBatch; ++i) x[i] = rv.pv[min(v0 + i * kFilterThreads, rv.nvec - 1)];
+#pragma unroll
+      for (int i = 0; i < kRowBatch; ++i) {
+        const bool ok = v0 + i * kFilterThreads < rv.nvec;
+#pragma unroll
+        for (int k = 0; k < VT::W; ++k) f(ok ? VT::get(x[i], k) : -INFINITY);
+      }
+    }
+    float e = -INFINITY, t;
+    if (threadIdx.x < 16 && rv.extra(threadIdx.x, t)) e = t;
+    f(e);
+  }
 };
-constexpr int kSegPerThread = 16;  // segment maxima a thread keeps in registers (rows of up to 4096 segments)
+constexpr int kSegPerThread = 4096 / kFilterThreads;  // segment maxima a thread keeps in registers (rows of up
+                                                      // to 4096 segments)
 
 struct MaxVisitor {  // the segment maxima, kSegPerThread per thread in registers
   const float (&mx)[kSegPerThread];
@@ -172,44 +201,48 @@ struct ListVisitor {  // a candidate list in LDS
 };
 
 __device__ __forceinline__ void hist_clear(unsigned long long* hist) {
-#pragma unroll
-  for (int c = 0; c < kHistCopies; ++c) hist[c * kHistStride + threadIdx.x] = 0ull;
+  for (int i = threadIdx.x; i < kHistCopies * kHistStride; i += kFilterThreads) hist[i] = 0ull;
 }
 __device__ __forceinline__ void hist_add(unsigned long long* hist, int bin, unsigned long long w) {
   atomicAdd(hist + (threadIdx.x & (kHistCopies - 1)) * kHistStride + bin, w);
 }
 
-// Find the bin B of hist[] (kFilterBins = kFilterThreads u64 weights, thread
-// t owning bin t) where, counting from the top bin down, base + (weight of
-// the bins above B) < target <= base + (weight of the bins from B up).
-// Returns B and adds the weight above B to base; -1 if the target exceeds the
-// total.  Whole workgroup.  s_u64 needs kFilterThreads / 64 + 1 slots.
+// Find the bin B of hist[] (kFilterBins u64 weights, thread t < kFilterBins
+// owning bin t) where, counting from the top bin down, base + (weight of the
+// bins above B) < target <= base + (weight of the bins from B up).  Returns B
+// and adds the weight above B to base; -1 if the target exceeds the total.
+// Whole workgroup.  s_u64 needs kFilterBins / 64 + 1 slots.
 __device__ __forceinline__ int find_bin(const unsigned long long* hist, double target, unsigned long long& base,
                                         unsigned long long* s_u64, int* s_bin) {
-  constexpr int NW = kFilterThreads / 64;
+  constexpr int NWB = kFilterBins / 64;  // the wavefronts that own bins
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool owner = tid < kFilterBins;  // whole wavefronts
   __syncthreads();  // the histogram is complete; earlier readers of s_u64 / s_bin are done
-  unsigned long long h = 0ull;
+  unsigned long long h = 0ull, suf = 0ull;
+  if (owner) {
 #pragma unroll
-  for (int c = 0; c < kHistCopies; ++c) h += hist[c * kHistStride + tid];
-  unsigned long long suf = h;  // suffix sums over the lanes of the wave, then over the waves
+    for (int c = 0; c < kHistCopies; ++c) h += hist[c * kHistStride + tid];
+    suf = h;  // suffix sums over the lanes of the wave, then over the waves
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const unsigned long long v = __shfl_down(suf, o);
-    if (lane + o < 64) suf += v;
+    for (int o = 1; o < 64; o <<= 1) {
+      const unsigned long long v = __shfl_down(suf, o);
+      if (lane + o < 64) suf += v;
+    }
+    if (lane == 0) s_u64[wave] = suf;
   }
   if (tid == 0) *s_bin = -1;
-  if (lane == 0) s_u64[wave] = suf;
   __syncthreads();
-  unsigned long long above = base + (suf - h);
-  for (int w = wave + 1; w < NW; ++w) above += s_u64[w];
-  if ((double)above < target && (double)(above + h) >= target) {
-    *s_bin = tid;
-    s_u64[NW] = above;
+  if (owner) {
+    unsigned long long above = base + (suf - h);
+    for (int w = wave + 1; w < NWB; ++w) above += s_u64[w];
+    if ((double)above < target && (double)(above + h) >= target) {
+      *s_bin = tid;
+      s_u64[NWB] = above;
+    }
   }
   __syncthreads();
   const int bin = *s_bin;
-  if (bin >= 0) base = s_u64[NW];
+  if (bin >= 0) base = s_u64[NWB];
   __syncthreads();  // s_u64, s_bin and hist are reused
   return bin;
 }
@@ -246,33 +279,46 @@ __device__ __forceinline__ uint32_t radix_select(const Vis& vis, uint32_t kmin, 
   return prefix;  // bf16: the low 16 bits stay 0, below every key of the selected value and above the next
 }
 
-// The same selection over a list of at most kFilterThreads values in LDS, one
-// per thread, by ranking: value v_i is the answer iff the weight of the
-// values > v_i is below the target and the weight of those >= v_i reaches it.
+// The same selection over a list of at most kRankMax values in LDS by
+// ranking: value v_i is the answer iff the weight of the values > v_i is
+// below the target and the weight of those >= v_i reaches it.  Value i is
+// ranked by the kRankParts adjacent lanes kRankParts i .. + kRankParts - 1,
+// each over every kRankParts-th value, and their sums combined by shuffles.
 template <bool MASS>
 __device__ __forceinline__ uint32_t rank_select(const float* vals, int n, uint32_t kmin, double target, float cs,
                                                 float shift, unsigned long long* wts, uint32_t* s_key) {
   const int tid = threadIdx.x;
+  const int i = tid / kRankParts, part = tid % kRankParts;
   __syncthreads();
-  float v = -INFINITY;
-  uint32_t kv = 0u;
   if (tid < n) {
-    v = vals[tid];
-    kv = order_key(v);
-    wts[tid] = (kv >= kmin) ? (MASS ? fixed_mass(exp2_hw(fmaf(v, cs, -shift))) : 1ull) : 0ull;
+    const float v = vals[tid];
+    wts[tid] = (order_key(v) >= kmin) ? (MASS ? fixed_mass(exp2_hw(fmaf(v, cs, -shift))) : 1ull) : 0ull;
   }
   if (tid == 0) *s_key = 0u;
   __syncthreads();
-  if (tid < n && kv >= kmin) {
-    unsigned long long gt = 0ull, eq = 0ull;
-    for (int i = 0; i < n; ++i) {
-      const float u = vals[i];
-      const unsigned long long w = wts[i];
+  float v = -INFINITY;
+  uint32_t kv = 0u;
+  if (i < n) {
+    v = vals[i];
+    kv = order_key(v);
+  }
+  const bool mine = i < n && kv >= kmin;
+  unsigned long long gt = 0ull, eq = 0ull;
+  if (mine) {
+    for (int k = part; k < n; k += kRankParts) {
+      const float u = vals[k];
+      const unsigned long long w = wts[k];
       gt += u > v ? w : 0ull;
       eq += u == v ? w : 0ull;
     }
-    if ((double)gt < target && (double)(gt + eq) >= target) *s_key = kv;  // equal values write the same key
   }
+#pragma unroll
+  for (int o = 1; o < kRankParts; o <<= 1) {  // every lane takes part
+    gt += __shfl_xor(gt, o);
+    eq += __shfl_xor(eq, o);
+  }
+  if (mine && part == 0 && (double)gt < target && (double)(gt + eq) >= target)
+    *s_key = kv;  // equal values write the same key
   __syncthreads();
   const uint32_t k = *s_key;
   __syncthreads();
@@ -365,29 +411,41 @@ __device__ __forceinline__ int gather_segments(const RowView<Elem>& rv, const fl
 
 // Selection over the whole row (no usable bound).  Elements are binned by
 // their distance below the row maximum in log2(e) units, d = shift - l c:
-// first only those within 16 bits of the maximum, 16 bins per bit (the
-// others are skipped at the cost of a compare, and in practice the threshold
-// lies there); if that window holds less than the target weight, then the
-// whole row with 4 bins per bit and everything beyond 64 bits in the lowest
-// bin.  Larger logits go to higher bins.  The bin where the cumulative weight
+// first only those within win bits of the maximum, 256 / win bins per bit
+// (the others are skipped at the cost of a compare); if that window holds
+// less than the target weight, then the whole row with 4 bins per bit and
+// everything beyond 64 bits in the lowest bin (directly when win >= 64).
+// For a mass target the caller derives win from a bound: the elements more
+// than D bits below the maximum weigh under V 2^-D together, so the threshold
+// lies within D bits once that is at most the mass the target leaves out.
+// Larger logits go to higher bins.  The bin where the cumulative weight
 // from the top reaches the target is gathered and selected exactly, with the
 // target less the weight above it.  If that bin overflows the candidate list,
 // radix selection runs on the keys of the whole row.  The candidate list is
 // left holding only that bin.
 //
+// In the window pass each wavefront appends the elements that pass the
+// window's pre-test to its queue in LDS (ballot and lane prefix count), and
+// bins them 64 at a time with every lane busy: a lane rarely holds a window
+// element, but nearly every step of the wavefront has one.  When no queue
+// overflowed, the queues still hold every window element, and the selected
+// bin is gathered from them instead of from the row.
+//
 // On return n_out is the number of candidates (the elements of the selected
 // bin) and base_out the weight above that bin, or n_out = -1 when the radix
 // selection over the row's keys ran instead.
 template <typename Elem, bool MASS>
-__device__ __forceinline__ uint32_t select_row(const RowVisitor<Elem>& all, uint32_t kmin, double target, float cs,
-                                               float shift, float* cand, unsigned long long* hist,
+__device__ __forceinline__ uint32_t select_row(const RowVisitor<Elem>& all, uint32_t kmin, double target, float win,
+                                               float cs, float shift, float* cand, unsigned long long* hist,
                                                unsigned long long* wts, unsigned long long* s_u64, int* s_bin,
-                                               uint32_t* s_key, int* s_cnt, int& n_out,
-                                               unsigned long long& base_out) {
+                                               uint32_t* s_key, int* s_cnt, int* s_over, float* stash,
+                                               int& n_out, unsigned long long& base_out) {
   n_out = -1;
+  const int lane = threadIdx.x & 63;
+  float* sw = stash + (threadIdx.x >> 6) * kStashW;  // this wavefront's queue
 #pragma unroll 1
-  for (int wide = 0; wide < 2; ++wide) {
-    const float per_bit = wide ? 4.f : 16.f;
+  for (int wide = win < 64.f ? 0 : 1; wide < 2; ++wide) {
+    const float per_bit = wide ? 4.f : 256.f / win;
     auto dbin = [&](float l) -> int {  // -1: outside the window
       const float d = -fmaf(l, cs, -shift) * per_bit;  // >= about 0; +inf for l = -inf
       if (!wide && !(d < 256.f)) return -1;
@@ -395,8 +453,9 @@ __device__ __forceinline__ uint32_t select_row(const RowVisitor<Elem>& all, uint
     };
     // Cheap pre-tests on the logit itself (one compare per element) with a
     // margin of 1/16 bit; the exact bin test follows for the few that pass.
-    const float lo_win = wide ? -INFINITY : (shift - 16.0625f) / cs;
+    const float lo_win = wide ? -INFINITY : (shift - (win + 0.0625f)) / cs;
     hist_clear(hist);
+    if (threadIdx.x == 0) *s_over = 0;
     auto process = [&](float l) {
       const int bin = dbin(l);
       if (bin >= 0 && order_key(l) >= kmin) {
@@ -405,9 +464,28 @@ __device__ __forceinline__ uint32_t select_row(const RowVisitor<Elem>& all, uint
       }
     };
     __syncthreads();
-    all([&](float l) {
-      if (l >= lo_win) process(l);
-    });
+    int qn = 0;  // elements queued by this wavefront (the same in all its lanes)
+    if (wide) {
+      all([&](float l) { process(l); });
+    } else {
+      int qd = 0;  // of which binned
+      all.uniform([&](float l) {
+        const bool in = l >= lo_win;
+        const unsigned long long m = __ballot(in);
+        if (m) {
+          const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          if (in) sw[(qn + rank) & (kStashW - 1)] = l;
+          qn += __popcll(m);
+          if (qn - qd >= 64) {  // fewer than 128 queued and unbinned: the ring never overwrites them
+            process(sw[(qd + lane) & (kStashW - 1)]);
+            qd += 64;
+          }
+        }
+      });
+      if (lane < qn - qd) process(sw[(qd + lane) & (kStashW - 1)]);
+      if (lane == 0 && qn > kStashW) *s_over = 1;
+    }
     unsigned long long base = 0ull;
     const int B = find_bin(hist, target, base, s_u64, s_bin);
     if (B < 0) continue;  // the window holds less than the target
@@ -416,19 +494,24 @@ __device__ __forceinline__ uint32_t select_row(const RowVisitor<Elem>& all, uint
     const float lo_b = (B == 0 && wide) ? -INFINITY : (shift - d_hi) / cs, hi_b = (shift - d_lo) / cs;
     if (threadIdx.x == 0) *s_cnt = 0;
     __syncthreads();
-    all([&](float l) {
+    auto put = [&](float l) {
       if (l >= lo_b && l <= hi_b && dbin(l) == B && order_key(l) >= kmin) {
         const int slot = atomicAdd(s_cnt, 1);
         if (slot < kFilterCand) cand[slot] = l;
       }
-    });
+    };
+    if (!wide && !*s_over) {  // (s_over is settled: find_bin synchronised the workgroup)
+      for (int i = lane; i < qn; i += 64) put(sw[i]);
+    } else {
+      all(put);
+    }
     __syncthreads();
     const int n = *s_cnt;
     const double rest = target - (double)base;
     if (n > kFilterCand) return radix_select<Elem, MASS>(all, kmin, target, cs, shift, 4, hist, s_u64, s_bin);
     n_out = n;
     base_out = base;
-    if (n <= kFilterThreads) return rank_select<MASS>(cand, n, kmin, rest, cs, shift, wts, s_key);
+    if (n <= kRankMax) return rank_select<MASS>(cand, n, kmin, rest, cs, shift, wts, s_key);
     return radix_select<Elem, MASS>(ListVisitor{cand, n}, kmin, rest, cs, shift, 4, hist, s_u64, s_bin);
   }
   return 0u;
@@ -439,7 +522,7 @@ template <typename Elem, bool MASS>
 __device__ __forceinline__ uint32_t select_list(const float* cand, int n, uint32_t kmin, double target, float cs,
                                                 float shift, unsigned long long* hist, unsigned long long* wts,
                                                 unsigned long long* s_u64, int* s_bin, uint32_t* s_key) {
-  if (n <= kFilterThreads) return rank_select<MASS>(cand, n, kmin, target, cs, shift, wts, s_key);
+  if (n <= kRankMax) return rank_select<MASS>(cand, n, kmin, target, cs, shift, wts, s_key);
   return radix_select<Elem, MASS>(ListVisitor{cand, n}, kmin, target, cs, shift, 4, hist, s_u64, s_bin);
 }
 
@@ -454,12 +537,13 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(
     int32_t j_begin, int32_t j_count, int32_t nsplit, const ReqRecord* __restrict__ records,
     const RowPartial* __restrict__ partials, const float* __restrict__ tmaxbuf, FilterRec* __restrict__ frec) {
   __shared__ unsigned long long hist[kHistCopies * kHistStride];
-  __shared__ unsigned long long wts[kFilterThreads];
+  __shared__ unsigned long long wts[kRankMax];
   __shared__ float cand[kFilterCand];
   __shared__ int qseg[kFilterSegList];
   __shared__ unsigned long long s_u64[kFilterThreads / 64 + 1];
   __shared__ double s_d[kFilterThreads / 64];
-  __shared__ int s_bin, s_cnt, s_nq;
+  __shared__ float stash[kFilterThreads / 64 * kStashW];
+  __shared__ int s_bin, s_cnt, s_nq, s_over;
   __shared__ uint32_t s_key;
   const int32_t j = j_begin + (int32_t)(blockIdx.x % j_count);
   const int32_t b = (int32_t)(blockIdx.x / j_count);
@@ -507,19 +591,18 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(
     } else {
       int nb;
       unsigned long long cb;
-      kappa = select_row<Elem, false>(all, 0u, (double)kb, cs, shift, cand, hist, wts, s_u64, &s_bin, &s_key, &s_cnt,
-                                      nb, cb);
+      kappa = select_row<Elem, false>(all, 0u, (double)kb, 16.f, cs, shift, cand, hist, wts, s_u64, &s_bin, &s_key, &s_cnt,
+                                      &s_over, stash, nb, cb);
     }
   }
   const float pb = top_p ? top_p[b] : 1.f;
   if (pb > 0.f && pb < 1.f) {
     // target: top_p times the mass kept by top-k (all of it without top-k)
-    double P;
-    if (kappa == 0u)
-      P = (double)pb * S * 0x1p+44;  // the row's sum in the fixed-point unit
-    else
-      P = (double)pb * (double)(ncand >= 0 ? fixed_total(ListVisitor{cand, ncand}, kappa, cs, shift, s_u64)
-                                           : fixed_total(all, kappa, cs, shift, s_u64));
+    const double total = kappa == 0u ? S * 0x1p+44  // the row's sum in the fixed-point unit
+                                     : (double)(ncand >= 0 ? fixed_total(ListVisitor{cand, ncand}, kappa, cs, shift,
+                                                                         s_u64)
+                                                           : fixed_total(all, kappa, cs, shift, s_u64));
+    const double P = (double)pb * total;
     if (ncand < 0) {
       const uint32_t bound =
           use_maxima ? radix_select<Elem, true>(maxima, kappa, P, cs, shift, kBoundLevels, hist, s_u64, &s_bin)
@@ -530,8 +613,15 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(
     if (ncand >= 0) {
       kp = select_list<Elem, true>(cand, ncand, kappa, P, cs, shift, hist, wts, s_u64, &s_bin, &s_key);
     } else {
-      kp = select_row<Elem, true>(all, kappa, P, cs, shift, cand, hist, wts, s_u64, &s_bin, &s_key, &s_cnt, nbin,
-                                  above_bin);
+      // window: D >= log2(2 V 2^44 / (total - P)) bits, so that V 2^-D (plus the
+      // truncation of up to V fixed-point units) stays within the left-out mass
+      // (capped at 16 bits: a wider bound comes from a peaked row, whose
+      // threshold normally lies within 16 bits of its maximum; if it does not,
+      // the pass over the whole row follows)
+      const double wb = log2(2.0 * (double)V * 0x1p+44 / (total - P)) + 0.0625;
+      const float win = (float)fmin(fmax(wb, 1.0), 16.0);
+      kp = select_row<Elem, true>(all, kappa, P, win, cs, shift, cand, hist, wts, s_u64, &s_bin, &s_key, &s_cnt,
+                                  &s_over, stash, nbin, above_bin);
     }
     if (kp) kappa = kp;
   }

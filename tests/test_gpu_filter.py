@@ -143,6 +143,30 @@ def test_filters_off_equal_unfiltered():
     np.testing.assert_array_equal(a.num_accepted, b.num_accepted)
 
 
+def test_signed_zeros_at_threshold():
+    # thresholds inside a large group of zeros of both signs: -0 and +0 are
+    # one value, so every zero is kept and counted in the kept mass
+    w = W.make([2] * 40, 4096, dtype=torch.bfloat16, temperature=1.0, q_mode="noise", q_sigma=0.8,
+               draft_mode="sample_q", seed=31, gen_seed=6031, device="cuda", name="signed zeros")
+    rng = np.random.default_rng(31)
+    base = np.full(4096, -6.0, np.float32)
+    base[:8] = 4.0
+    base[8:1508] = 0.0
+    base[1508:3008] = -0.0
+    rows = np.stack([rng.permutation(base) for _ in range(w.logits.shape[0])])
+    w.logits = torch.from_numpy(rows).to(torch.bfloat16).to(w.logits.device).contiguous()
+    top_k = rng.choice([0, 8, 9, 500, 2000, 3008, 3009, 4095], size=w.B)
+    top_p = rng.choice([1.0, 0.5, 0.9, 0.99, 0.999], size=w.B)
+    w = w.with_filters(top_k.tolist(), top_p.tolist())
+    _say(f"signed zeros: B={w.B} V={w.V}")
+    o = run_oracle(w)
+    for _ in range(3):  # ties of equal values once raced here: repeat
+        g = run_gpu(w, want_p=True)
+        rep = compare(g, o, w)
+        compare_p(g, o)
+        assert rep["flagged"] == 0
+
+
 def test_top_k_one_is_greedy_like():
     # top-k = 1 leaves only the argmax (and its exact ties): every emitted
     # extra token is a row maximum of its logits

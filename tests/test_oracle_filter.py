@@ -91,6 +91,19 @@ def test_ties_are_kept_together():
     assert _support(p) == {0}
 
 
+def test_signed_zeros_are_one_value():
+    # -0 and +0 are the same logit: a threshold among zeros keeps both signs,
+    # and the result equals that of the row with every zero positive
+    l = np.array([2.0, 0.0, -0.0, 0.0, -0.0, -0.0, -3.0, 1.0])
+    pos = l + 0.0  # the same values, no negative zero (-0 + +0 = +0)
+    assert np.signbit(l).sum() == 4 and np.signbit(pos).sum() == 1
+    for k, tp in ((3, 1.0), (4, 1.0), (0, 0.7), (0, 0.9), (5, 0.8)):
+        p, _ = oracle.filtered_probs_row(l, 1.0, top_k=k, top_p=tp)
+        q, _ = oracle.filtered_probs_row(pos, 1.0, top_k=k, top_p=tp)
+        np.testing.assert_array_equal(p, q)
+        assert _support(p) >= {1, 2, 3, 4, 5}  # every zero kept
+
+
 def test_degenerate_settings():
     rng = np.random.default_rng(9)
     l = rng.standard_normal(50) * 3

@@ -109,8 +109,8 @@ __device__ __forceinline__ void race_span(const Elem* __restrict__ lrow, const f
   for (int i = 0; i < NG; ++i) {
     const int32_t G = G0 + tid + i * kRaceThreads;
     if (FULL || G < Gfull) {
-      lw[i] = reinterpret_cast<const typename R4::T*>(lrow)[G];
-      if (kQ) qw[i] = reinterpret_cast<const float4*>(qrow)[G];
+      lw[i] = stream_load(reinterpret_cast<const typename R4::T*>(lrow) + G);
+      if (kQ) qw[i] = stream_load(reinterpret_cast<const float4*>(qrow) + G);
     }
   }
 #pragma unroll

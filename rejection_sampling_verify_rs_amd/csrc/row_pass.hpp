@@ -271,7 +271,7 @@ __device__ __forceinline__ void chunk_task(const Elem* __restrict__ logits, cons
   uint4 data[NV];
   if (full) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) data[i] = pv[v0 + tid + i * kRowThreads];
+    for (int i = 0; i < NV; ++i) data[i] = stream_load(pv + v0 + tid + i * kRowThreads);
   } else {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {

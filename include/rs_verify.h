@@ -245,15 +245,14 @@ rs_status rs_verify_greedy(const void* target_logits, rs_dtype logits_dtype,
  * <= max_nodes the depth (a node with no parent has depth 0); a request whose
  * tree breaks these rules (too many nodes, a parent after its child, a token
  * out of range, a node of depth >= max_depth) gets -1 rows and
- * num_accepted = -1.  V <= RS_TREE_MAX_VOCAB.  One workgroup per request
- * walks the tree, streaming only the rows on its accepted path and the stop
- * row; the final race of random requests is spread over the GPU.
+ * num_accepted = -1.  One workgroup per request walks the tree, streaming
+ * only the rows on its accepted path and the stop row; the final race of
+ * random requests is spread over the GPU.
  *   workspace  >= rs_verify_tree_workspace_size(B, V) bytes, 16-byte aligned
  *              (RS_ERR_WORKSPACE otherwise); calls sharing one workspace must
  *              not overlap.
  * Ownership, asynchrony and error reporting as for rs_verify. */
 #define RS_MAX_TREE_NODES 64
-#define RS_TREE_MAX_VOCAB 524288
 size_t rs_verify_tree_workspace_size(int32_t batch, int32_t vocab);
 rs_status rs_verify_tree(const void* target_logits, rs_dtype logits_dtype, const int32_t* node_tokens,
                          const int32_t* node_parents, const int32_t* cu_num_nodes, const float* temperature,

@@ -21,14 +21,11 @@ namespace rsv {
 
 // Block-wide exponential race over one row (see race_group); returns the
 // packed winner (key bits, ~x) or 0 when no residual value is positive.
-// excl_bits (NULL: none) is a bitmap of tokens taken out of the race
-// (bit x & 31 of word x >> 5): their weight is 0.
 template <typename Elem, int NT>
 __device__ __forceinline__ unsigned long long race_row(const Elem* __restrict__ lrow, const float* __restrict__ qrow,
                                                        int mode, int32_t exclude, float cs, float shift,
                                                        float inv_sum, uint32_t k0, uint32_t k1, uint32_t j,
-                                                       uint32_t b, int32_t V, unsigned long long* s_u,
-                                                       const uint32_t* excl_bits = nullptr) {
+                                                       uint32_t b, int32_t V, unsigned long long* s_u) {
   constexpr int NB = 4;  // groups of four tokens per thread per batch, double-buffered
   using R4 = Raw4<Elem>;
   const int tid = threadIdx.x;
@@ -65,11 +62,6 @@ __device__ __forceinline__ unsigned long long race_row(const Elem* __restrict__ 
           qv[3] = has_q ? qw[buf][i].w : 0.f;
         } else {
           load_group_scalar(lrow, qrow, G, V, l, qv);
-        }
-        if (excl_bits) {  // tokens 4G .. 4G+3 share word G >> 3, bits 4 (G & 7) .. 4 (G & 7) + 3
-          const uint32_t w = excl_bits[G >> 3] >> ((G & 7) << 2);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) l[k] = ((w >> k) & 1u) ? -INFINITY : l[k];
         }
         race_group(l, qv, mode, exclude, cs, shift, inv_sum, -INFINITY, k0, k1, j, b, G, best_key, best_x);
       }

@@ -619,7 +619,6 @@ rs_status rs_verify_tree(const void* target_logits, rs_dtype logits_dtype, const
   if (batch == 0) return RS_OK;
   if (max_nodes > RS_MAX_TREE_NODES || max_depth > max_nodes || (int64_t)total_nodes > (int64_t)batch * max_nodes)
     return RS_ERR_INVALID_ARG;
-  if (vocab > RS_TREE_MAX_VOCAB) return RS_ERR_UNSUPPORTED;
   if (!target_logits || !cu_num_nodes || !temperature || !output_token_ids || !num_accepted ||
       (max_depth > 0 && !accepted_nodes) || (total_nodes > 0 && (!node_tokens || !node_parents)))
     return RS_ERR_INVALID_ARG;

@@ -31,7 +31,6 @@
 #include "common.hpp"
 #include "philox.hpp"
 #include "race.hpp"
-#include "request_path.hpp"
 #include "row_pass.hpp"
 
 namespace rsv {

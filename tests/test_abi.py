@@ -237,7 +237,7 @@ def _call_tree(lib, **kw):
     (dict(max_nodes=65, max_depth=4), rs.RS_ERR_INVALID_ARG),   # RS_MAX_TREE_NODES = 64
     (dict(max_depth=9), rs.RS_ERR_INVALID_ARG),                 # deeper than max_nodes
     (dict(N=17), rs.RS_ERR_INVALID_ARG),                        # N > B * max_nodes
-    (dict(V=524289), rs.RS_ERR_UNSUPPORTED),
+    (dict(V=0), rs.RS_ERR_INVALID_ARG),
     (dict(dtype=3), rs.RS_ERR_UNSUPPORTED),
     (dict(tok=None), rs.RS_ERR_INVALID_ARG),
     (dict(path=None), rs.RS_ERR_INVALID_ARG),

@@ -60,6 +60,8 @@ CASES = [
     ("wide fp32 V=32000 mixed", 40, 32000, torch.float32, 3, (8, 3, 1), 64, [0.0, 0.8, 1.0, -1.0] * 10),
     ("deep bf16 V=50000", 24, 50000, torch.bfloat16, 8, (2, 2, 2, 1, 1, 1, 1, 1), 48, 1.0),
     ("tiny V=7 fp32", 50, 7, torch.float32, 3, (3, 2, 1), 20, 0.9),
+    # a vocabulary of more than 2^19 tokens, odd size: ragged last race chunk
+    ("big vocab bf16 V=600001", 3, 600001, torch.bfloat16, 3, (3, 2, 1), 16, ("uniform", 0.6, 1.2)),
 ]
 
 

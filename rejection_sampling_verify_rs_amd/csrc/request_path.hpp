@@ -79,6 +79,8 @@ __device__ __forceinline__ unsigned long long race_row(const Elem* __restrict__ 
   return block_reduce<NT>(pack_key(best_key, best_x), s_u, MaxOp());
 }
 
+constexpr int kRequestNVP = 8;  // 16-byte vectors per thread per statistics pass
+
 template <typename Elem, int NT>
 __global__ __launch_bounds__(NT) void request_kernel(
     const Elem* __restrict__ logits, const float* __restrict__ q, const int32_t* __restrict__ draft,
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(NT) void request_kernel(
     int32_t max_k, int32_t V, uint64_t seed, int32_t* __restrict__ out, int32_t* __restrict__ num_accepted,
     double* __restrict__ dbg_p) {
   constexpr int NW = NT / 64;
-  constexpr int NVP = 8;  // 16-byte vectors per thread per statistics pass
+  constexpr int NVP = kRequestNVP;
   __shared__ float s_f[NW];
   __shared__ int s_i[NW];
   __shared__ double s_d[NW];

@@ -46,7 +46,17 @@ namespace rsv {
 
 constexpr size_t kRegionAlign = 256;
 constexpr int kPathRequest = 1, kPathPhased = 2, kPathStream = 3;
-constexpr int64_t kStreamMinTasksPerPosition = 1024;
+// Automatic path choice, from timings of every path over batch sizes 1-512,
+// draft lengths 3-8 and vocabularies of 1024-151936 on one MI355X:
+//  * per-request when the batch is tiny and each request's serial walk is at
+//    most kRequestMaxSteps batches of loads (the others pay ~30 us of launches);
+//  * stream when rows split into 16-vector chunks give at least
+//    kStreamMinTasksPerPosition row tasks per position (fewer, or smaller
+//    chunks, leave the stream kernel's decisions too little work to overlap);
+//  * phased otherwise.
+constexpr int64_t kStreamMinTasksPerPosition = 512;
+constexpr int kRequestMaxBatch = 8;
+constexpr int kRequestMaxSteps = 10;
 constexpr int kTargetBlocks = 2048;  // enough workgroups to fill 256 CUs several times
 constexpr int kMaxPhases = 4;
 
@@ -255,9 +265,18 @@ static bool make_plan(int32_t B, int32_t D, int32_t max_k, int32_t V, rs_dtype d
     p.path = kPathPhased;  // full probabilities need every row (one phase); filters run per phase
   else if (force_path)
     p.path = force_path == 1 ? kPathRequest : force_path == 3 ? kPathStream : kPathPhased;
-  else  // the stream path needs enough row tasks per position for decisions to land before later rows start
-    p.path = (int64_t)B * p.nsplit >= kStreamMinTasksPerPosition ? kPathStream : kPathPhased;
+  else
+    p.path = kPathPhased;  // chosen below
   p.request_nt = V >= 65536 ? 1024 : 256;
+  if (!force_path && !(dbg && dbg->probs) && !filtered) {
+    const int64_t per_pass = (int64_t)p.request_nt * kRequestNVP;
+    const int64_t steps = (int64_t)(max_k + 1) * ((p.nvec_max + per_pass - 1) / per_pass);
+    if (B <= kRequestMaxBatch && steps <= kRequestMaxSteps)
+      p.path = kPathRequest;
+    else
+      p.path = (p.row_nv == kSegVectors && (int64_t)B * p.nsplit >= kStreamMinTasksPerPosition) ? kPathStream
+                                                                                             : kPathPhased;
+  }
   // Phases: position ranges [bounds[i], bounds[i+1]).  A request decided in
   // one phase never has the rows of later phases read.  Full probabilities
   // need every row, so they force one phase.

@@ -111,8 +111,11 @@ typedef struct rs_debug {
    * does not depend on these (the parity tests check that). */
   int32_t row_vectors_per_thread;
   int32_t race_tokens_per_thread;
-  /* 0 = automatic: the stream path when B times the V-chunks per row is at
-   * least 1024, else the phased split path.  1 = per-request path: one
+  /* 0 = automatic: the per-request path for batches of at most 8 requests
+   * whose rows take at most 10 load passes per request in all; else the
+   * stream path when rows split into 16-vector chunks give B times the
+   * chunks per row of at least 512; else the phased split path.  1 =
+   * per-request path: one
    * workgroup per request walks its rows in order and stops at the first
    * rejection.  2 = phased split path: each phase spreads every active
    * request's rows across the whole GPU, then scans.  3 = stream path: one

@@ -292,8 +292,17 @@ __device__ __forceinline__ void stream_race_task(const StreamArgs<Elem>& a, int3
   }
 }
 
+// Wavefronts per SIMD: the kernel's time is the sum of its tasks' durations
+// over the resident workgroups.  With bf16 logits 5 rather than 4 fit in 96
+// VGPRs without spills and took the call from 122 to 117 us at B=256 K=8
+// V=151936 (6 spill and are slower); the fp32 race chunk would spill at 5.
+template <typename Elem>
+constexpr int stream_waves_per_simd() {
+  return sizeof(Elem) == 2 ? 5 : 4;
+}
+
 template <typename Elem, int NV, int TPT>
-__global__ __launch_bounds__(kRowThreads) void stream_kernel(StreamArgs<Elem> a) {
+__global__ __launch_bounds__(kRowThreads, stream_waves_per_simd<Elem>()) void stream_kernel(StreamArgs<Elem> a) {
   __shared__ int32_t s_word;
   const int64_t t = blockIdx.x;
   int64_t k = t;  // row task index

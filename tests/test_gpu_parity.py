@@ -128,6 +128,26 @@ def test_paths_and_phases_full_size(n, path, phases):
     compare_p(g, o)
 
 
+@pytest.mark.parametrize("ks,V,want", [([4], 1024, 1), ([5] * 8, 1024, 1), ([4] * 16, 32000, 2),
+                                       ([8] * 96, 151936, 2), ([8] * 128, 151936, 3), ([3] * 512, 32000, 3)])
+def test_automatic_path_choice(ks, V, want):
+    """The automatic rule picks the per-request path for tiny batches with
+    short walks, the stream path from B x chunks per row >= 512 (16-vector
+    chunks), the phased split otherwise; the chosen path matches the oracle."""
+    w = W.make(ks, V, dtype=torch.bfloat16, logit_std=4.0, temperature=("uniform", 0.3, 1.2), q_mode="noise",
+               q_sigma=0.8, seed=41, gen_seed=4100 + len(ks), device="cuda")
+    d = rs.Debug()
+    out, n = rs.verify(w.logits, w.draft_probs, w.draft_token_ids, w.cu_num_draft_tokens, w.temperature,
+                       seed=w.seed, max_k=w.max_k, debug=d)
+    torch.cuda.synchronize()
+    _say(f"B={w.B} K={ks[0]} V={V}: path {d.path_taken}")
+    assert d.path_taken == want
+    o = run_oracle(w)
+    ok = ~o.near_tie
+    np.testing.assert_array_equal(out.cpu().numpy()[ok], o.tokens[ok])
+    np.testing.assert_array_equal(n.cpu().numpy()[ok], o.num_accepted[ok])
+
+
 def test_rerun_is_bit_identical():
     w = W.config(5, device="cuda")
     _say("workload 5 twice")

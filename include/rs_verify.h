@@ -113,8 +113,9 @@ typedef struct rs_debug {
   int32_t race_tokens_per_thread;
   /* 0 = automatic: the per-request path for batches of at most 8 requests
    * whose rows take at most 10 load passes per request in all; else the
-   * stream path when rows split into 16-vector chunks give B times the
-   * chunks per row of at least 512; else the phased split path.
+   * stream path when the logits total at most 128 MB or rows split into
+   * 16-vector chunks give B times the chunks per row of at least 512; else
+   * the phased split path.
    * 1 = per-request path: one workgroup per request walks its rows in order
    * and stops at the first rejection.  2 = phased split path: each phase
    * spreads every active

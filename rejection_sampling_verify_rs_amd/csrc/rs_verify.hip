@@ -50,11 +50,14 @@ constexpr int kPathRequest = 1, kPathPhased = 2, kPathStream = 3;
 // draft lengths 3-8 and vocabularies of 1024-151936 on one MI355X:
 //  * per-request when the batch is tiny and each request's serial walk is at
 //    most kRequestMaxSteps batches of loads (the others pay ~30 us of launches);
-//  * stream when rows split into 16-vector chunks give at least
-//    kStreamMinTasksPerPosition row tasks per position (fewer, or smaller
-//    chunks, leave the stream kernel's decisions too little work to overlap);
-//  * phased otherwise.
+//  * stream, with rows in 16-vector chunks, when the logits total at most
+//    kStreamSmallBytes (launch-bound: 3 launches against the phased path's 6)
+//    or the chunks give at least kStreamMinTasksPerPosition row tasks per
+//    position;
+//  * phased otherwise (mid-size batches, where too few row tasks per position
+//    leave the stream kernel's decisions too little work to overlap).
 constexpr int64_t kStreamMinTasksPerPosition = 512;
+constexpr int64_t kStreamSmallBytes = 128ll << 20;
 constexpr int kRequestMaxBatch = 8;
 constexpr int kRequestMaxSteps = 10;
 constexpr int kTargetBlocks = 2048;  // enough workgroups to fill 256 CUs several times
@@ -271,11 +274,19 @@ static bool make_plan(int32_t B, int32_t D, int32_t max_k, int32_t V, rs_dtype d
   if (!force_path && !(dbg && dbg->probs) && !filtered) {
     const int64_t per_pass = (int64_t)p.request_nt * kRequestNVP;
     const int64_t steps = (int64_t)(max_k + 1) * ((p.nvec_max + per_pass - 1) / per_pass);
-    if (B <= kRequestMaxBatch && steps <= kRequestMaxSteps)
+    const int64_t split16 = nsplit_for(p.nvec_max, kSegVectors);  // row tasks per row in 16-vector chunks
+    const bool small = R * (int64_t)V * (dt == RS_BF16 ? 2 : 4) <= kStreamSmallBytes;
+    if (B <= kRequestMaxBatch && steps <= kRequestMaxSteps) {
       p.path = kPathRequest;
-    else
-      p.path = (p.row_nv == kSegVectors && (int64_t)B * p.nsplit >= kStreamMinTasksPerPosition) ? kPathStream
-                                                                                             : kPathPhased;
+    } else if (small || (p.row_nv == kSegVectors && (int64_t)B * split16 >= kStreamMinTasksPerPosition)) {
+      p.path = kPathStream;
+    } else {
+      p.path = kPathPhased;
+    }
+  }
+  if (p.path == kPathStream && !force_nv) {  // the stream path's row tasks: 16-vector chunks
+    p.row_nv = kSegVectors;
+    p.nsplit = nsplit_for(p.nvec_max, kSegVectors);
   }
   // Phases: position ranges [bounds[i], bounds[i+1]).  A request decided in
   // one phase never has the rows of later phases read.  Full probabilities

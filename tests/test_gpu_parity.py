@@ -128,12 +128,14 @@ def test_paths_and_phases_full_size(n, path, phases):
     compare_p(g, o)
 
 
-@pytest.mark.parametrize("ks,V,want", [([4], 1024, 1), ([5] * 8, 1024, 1), ([4] * 16, 32000, 2),
-                                       ([8] * 96, 151936, 2), ([8] * 128, 151936, 3), ([3] * 512, 32000, 3)])
+@pytest.mark.parametrize("ks,V,want", [([4], 1024, 1), ([5] * 8, 1024, 1), ([4] * 16, 32000, 3), ([8] * 32, 151936, 3),
+                                       ([8] * 64, 151936, 2), ([8] * 96, 151936, 2), ([8] * 128, 151936, 3),
+                                       ([3] * 512, 32000, 3)])
 def test_automatic_path_choice(ks, V, want):
     """The automatic rule picks the per-request path for tiny batches with
-    short walks, the stream path from B x chunks per row >= 512 (16-vector
-    chunks), the phased split otherwise; the chosen path matches the oracle."""
+    short walks; the stream path when the logits total at most 128 MB or
+    from B x chunks per row >= 512 (16-vector chunks); the phased split
+    otherwise.  The chosen path matches the oracle."""
     w = W.make(ks, V, dtype=torch.bfloat16, logit_std=4.0, temperature=("uniform", 0.3, 1.2), q_mode="noise",
                q_sigma=0.8, seed=41, gen_seed=4100 + len(ks), device="cuda")
     d = rs.Debug()

@@ -126,8 +126,10 @@ typedef struct rs_debug {
    * selects the split path. */
   int32_t sampling_path;
   /* Phases of the split path, as the draft positions where phases end.
-   * phase_ends[0] == 0: automatic; phase_ends[0] < 0: one phase (every row
-   * is read); otherwise strictly increasing ends P1 < P2 < ..., stopping at
+   * phase_ends[0] == 0: automatic (one phase for a filtered call whose
+   * logits total at most 256 MB, else about the first third of the
+   * positions, then the rest); phase_ends[0] < 0: one phase (every row is
+   * read); otherwise strictly increasing ends P1 < P2 < ..., stopping at
    * the first entry that is 0 or >= max_k + 1 (the last phase always ends at
    * max_k + 1).  At most four phases.  On the stream path phase_ends[0] > 0
    * is the number of positions streamed before race tasks start to

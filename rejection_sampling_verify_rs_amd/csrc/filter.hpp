@@ -517,6 +517,98 @@ __device__ __forceinline__ uint32_t select_row(const RowVisitor<Elem>& all, uint
   return 0u;
 }
 
+// Whole-row selection for bf16 logits by exact value.  A bf16 row holds few
+// distinct values near its maximum, so one pass counts the elements of each
+// of the kValueBins values just below the row maximum (u32 LDS counters, no
+// per-element mass); the weight of a bin is then count x (1 or the
+// fixed-point mass of its value), and a scan from the top finds the value
+// where the cumulative weight reaches the target.  Every element of a bin
+// has that value, so the weights are exactly the per-element sums the
+// selection above forms, and ties stay together; the kept mass is the
+// weight above the threshold's bin plus the bin.  Elements below lo_pre
+// (the top-p window's pre-test; -inf for counts) are not counted: they lie in
+// no bin that can hold the threshold.  Returns the 32-bit order key of the
+// threshold value, with its bin's weight and the weight above it, or 0 when
+// the target is not reached within the bins (the caller then selects with
+// select_row).
+constexpr int kValueBins = kFilterThreads / 64 * kStashW;  // 4096: the queues' LDS, as u32 counters
+
+__device__ __forceinline__ uint32_t bf16_key(float l) {  // order key of a widened bf16 value; -0 is +0
+  uint32_t u = __float_as_uint(l) >> 16;
+  u = u == 0x8000u ? 0u : u;
+  return (u & 0x8000u) ? (~u & 0xFFFFu) : (u | 0x8000u);
+}
+__device__ __forceinline__ float bf16_value(uint32_t key) {
+  const uint32_t u = (key & 0x8000u) ? (key & 0x7FFFu) : (~key & 0xFFFFu);
+  return __uint_as_float(u << 16);
+}
+
+template <bool MASS>
+__device__ __forceinline__ uint32_t select_value_bins(const RowVisitor<uint16_t>& all, float rowmax, uint32_t kmin,
+                                                      double target, float lo_pre, float cs, float shift,
+                                                      uint32_t* cnt, unsigned long long* s_u64, int* s_bin,
+                                                      unsigned long long* s_vb, unsigned long long& bin_out,
+                                                      unsigned long long& above_out) {
+  constexpr int NW = kFilterThreads / 64;
+  constexpr int PER = kValueBins / kFilterThreads;  // bins per thread: thread t owns [t PER, t PER + PER)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t ktop = bf16_key(rowmax);
+  __syncthreads();  // earlier users of the LDS are done
+  for (int i = tid; i < kValueBins; i += kFilterThreads) cnt[i] = 0u;
+  if (tid == 0) *s_bin = -1;
+  __syncthreads();
+  all([&](float l) {
+    if (l >= lo_pre) {
+      const uint32_t d = ktop - bf16_key(l);  // bin 0 = the maximum (no key exceeds ktop)
+      if (d < (uint32_t)kValueBins) atomicAdd(cnt + d, 1u);
+    }
+  });
+  __syncthreads();
+  unsigned long long w[PER], sum = 0ull;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const uint32_t d = (uint32_t)(tid * PER + i);
+    const uint32_t c = cnt[d];
+    w[i] = 0ull;
+    if (c && d <= ktop) {
+      const float v = bf16_value(ktop - d);
+      if (order_key(v) >= kmin) w[i] = MASS ? (unsigned long long)c * fixed_mass(exp2_hw(fmaf(v, cs, -shift))) : c;
+    }
+    sum += w[i];
+  }
+  // exclusive prefix of the thread sums in thread order (top bins first)
+  unsigned long long incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) s_u64[wave] = incl;
+  __syncthreads();
+  unsigned long long above = incl - sum;
+  for (int q = 0; q < wave; ++q) above += s_u64[q];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if ((double)above < target && (double)(above + w[i]) >= target) {  // one bin at most
+      *s_bin = tid * PER + i;
+      s_vb[0] = w[i];
+      s_vb[1] = above;
+    }
+    above += w[i];
+  }
+  __syncthreads();
+  const int bin = *s_bin;
+  uint32_t key = 0u;
+  if (bin >= 0) {
+    bin_out = s_vb[0];
+    above_out = s_vb[1];
+    key = order_key(bf16_value(ktop - (uint32_t)bin));
+  }
+  __syncthreads();  // s_u64, s_bin, s_vb and the counters are reused
+  (void)NW;
+  return key;
+}
+
 // Select over the candidate list: ranking for short lists, radix otherwise.
 template <typename Elem, bool MASS>
 __device__ __forceinline__ uint32_t select_list(const float* cand, int n, uint32_t kmin, double target, float cs,
@@ -545,6 +637,8 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(
   __shared__ float stash[kFilterThreads / 64 * kStashW];
   __shared__ int s_bin, s_cnt, s_nq, s_over;
   __shared__ uint32_t s_key;
+  __shared__ float s_f[kFilterThreads / 64];
+  __shared__ unsigned long long s_vb[2];
   const int32_t j = j_begin + (int32_t)(blockIdx.x % j_count);
   const int32_t b = (int32_t)(blockIdx.x / j_count);
   const int32_t s = cu[b], e = cu[b + 1];
@@ -575,6 +669,13 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(
   double S;
   merge_random(partials + row * nsplit, nsplit, shift, S);
 
+  unsigned long long kept_fixed = 0ull;  // top-p by value bins: the kept mass in the fixed-point unit (0: not used)
+  auto row_max = [&]() {  // the row's maximum, from the segment maxima (they cover every element)
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kSegPerThread; ++i) m = fmaxf(m, mx[i]);
+    return block_reduce<kFilterThreads>(m, s_f, MaxOp());
+  };
   int nbin = -1;                 // top-p over the row: elements of the threshold's bin in cand[0 .. nbin)
   unsigned long long above_bin = 0ull;  // and the fixed-point mass above that bin
   int ncand = -1;       // candidate list: every element >= its bound is in cand[0 .. ncand) (-1: none)
@@ -590,9 +691,16 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(
       kappa = select_list<Elem, false>(cand, ncand, 0u, (double)kb, cs, shift, hist, wts, s_u64, &s_bin, &s_key);
     } else {
       int nb;
-      unsigned long long cb;
-      kappa = select_row<Elem, false>(all, 0u, (double)kb, 16.f, cs, shift, cand, hist, wts, s_u64, &s_bin, &s_key, &s_cnt,
-                                      &s_over, stash, nb, cb);
+      unsigned long long cb, ab;
+      kappa = 0u;
+      if constexpr (sizeof(Elem) == 2) {
+        if (use_maxima)
+          kappa = select_value_bins<false>(all, row_max(), 0u, (double)kb, -INFINITY, cs, shift,
+                                           reinterpret_cast<uint32_t*>(stash), s_u64, &s_bin, s_vb, cb, ab);
+      }
+      if (!kappa)
+        kappa = select_row<Elem, false>(all, 0u, (double)kb, 16.f, cs, shift, cand, hist, wts, s_u64, &s_bin, &s_key,
+                                        &s_cnt, &s_over, stash, nb, cb);
     }
   }
   const float pb = top_p ? top_p[b] : 1.f;
@@ -620,8 +728,18 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(
       // the pass over the whole row follows)
       const double wb = log2(2.0 * (double)V * 0x1p+44 / (total - P)) + 0.0625;
       const float win = (float)fmin(fmax(wb, 1.0), 16.0);
-      kp = select_row<Elem, true>(all, kappa, P, win, cs, shift, cand, hist, wts, s_u64, &s_bin, &s_key, &s_cnt,
-                                  &s_over, stash, nbin, above_bin);
+      kp = 0u;
+      if constexpr (sizeof(Elem) == 2) {
+        if (use_maxima) {
+          unsigned long long bw, ab;
+          kp = select_value_bins<true>(all, row_max(), kappa, P, (shift - (win + 0.0625f)) / cs, cs, shift,
+                                       reinterpret_cast<uint32_t*>(stash), s_u64, &s_bin, s_vb, bw, ab);
+          if (kp) kept_fixed = ab + bw;
+        }
+      }
+      if (!kp)
+        kp = select_row<Elem, true>(all, kappa, P, win, cs, shift, cand, hist, wts, s_u64, &s_bin, &s_key, &s_cnt,
+                                    &s_over, stash, nbin, above_bin);
     }
     if (kp) kappa = kp;
   }
@@ -638,6 +756,8 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(
   if (ncand >= 0) {
     ListVisitor{cand, ncand}(add);
     acc = block_reduce<kFilterThreads>(acc, s_d, SumOp());
+  } else if (kept_fixed) {
+    acc = (double)kept_fixed * 0x1p-44;
   } else if (nbin >= 0 && kappa) {
     acc = (double)(above_bin + fixed_total(ListVisitor{cand, nbin}, kappa, cs, shift, s_u64)) * 0x1p-44;
   } else {

@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kRaceThreads) void tree_race_kernel(
   if (Gfull > 0) {  // unconditional loads (index clamped into the vector part): all in flight together
 #pragma unroll
     for (int i = 0; i < NG; ++i)
-      lw[i] = reinterpret_cast<const typename R4::T*>(lrow)[min(G0 + tid + i * kRaceThreads, Gfull - 1)];
+      lw[i] = stream_load(reinterpret_cast<const typename R4::T*>(lrow) + min(G0 + tid + i * kRaceThreads, Gfull - 1));
   }
   float best_key = 0.f;
   int32_t best_x = INT_MAX;

@@ -98,6 +98,21 @@ def test_workload_with_filters(n):
     assert rep["flagged"] <= 1
 
 
+@pytest.mark.parametrize("n,tp", [(4, 0.9), (5, 0.95), (3, 0.8)])
+def test_top_p_alone_full_size(n, tp):
+    # top-p without top-k at full size: most rows keep hundreds to thousands of
+    # tokens, so their thresholds come from the whole-row selection (by exact
+    # value for bf16 logits)
+    w = W.config(n, device="cuda").with_filters(None, tp)
+    _say(f"workload {n} + top_p {tp}: B={w.B} V={w.V}")
+    g = run_gpu(w, want_p=True)
+    o = run_oracle(w)
+    rep = compare(g, o, w)
+    worst = compare_p(g, o)
+    _say(f"workload {n} top_p {tp}: flagged {rep['flagged']}/{rep['requests']}, max p' rel err {worst:.3e}")
+    assert rep["flagged"] <= 2
+
+
 def test_filtered_probs_match_oracle():
     w = _case("probs", [2, 0, 3, 1] * 3, 3000, torch.bfloat16, "noise", ("uniform", 0.5, 1.5), 26)
     g = run_gpu(w, want_probs=True)

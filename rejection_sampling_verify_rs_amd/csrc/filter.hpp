@@ -31,7 +31,9 @@
 //   * S' is summed over the list.
 // When no bound can be formed (k above the number of segments, segment maxima
 // lighter than the top-p target) or the list overflows, the selection runs
-// over the whole row, re-read from memory (select_row).
+// over the whole row, re-read from memory: for bf16 logits by exact value
+// (select_value_bins), else -- or when the threshold lies below the values
+// that method counts -- by distance bins (select_row).
 #pragma once
 
 #include "common.hpp"

@@ -68,3 +68,64 @@ def test_random_parity_sweep(seed):
         o = run_oracle(w)
         compare(g, o, w)
         compare_p(g, o)
+
+
+def _random_trees(rng):
+    """Ragged random trees (node i's parent uniform over the earlier nodes and
+    the prefix), children's tokens mostly near the top of their parent's row,
+    sometimes random or repeated; mixed greedy / random temperatures."""
+    V = int(rng.choice([7, 1000, 32000, 151936]))
+    B = int(rng.integers(1, 40 if V > 32000 else 100))
+    max_nodes = int(rng.choice([8, 20, 64]))
+    dtype = torch.bfloat16 if rng.random() < 0.7 else torch.float32
+    counts = rng.integers(0, max_nodes + 1, size=B)
+    parents, tokens, depth_max = [], [], 0
+    rows = []
+    for b in range(B):
+        n = int(counts[b])
+        par = [int(rng.integers(-1, i)) for i in range(n)]
+        dep = []
+        for i, p_ in enumerate(par):
+            dep.append(0 if p_ < 0 else dep[p_] + 1)
+        depth_max = max([depth_max] + [d + 1 for d in dep])
+        lg = torch.from_numpy((rng.standard_normal((n + 1, V)) * float(rng.choice([1.0, 3.0]))).astype(np.float32))
+        tk = []
+        for i, p_ in enumerate(par):
+            r = lg[p_ + 1]
+            u = rng.random()
+            if u < 0.6:
+                tk.append(int(torch.topk(r, min(3, V)).indices[int(rng.integers(0, min(3, V)))]))
+            elif u < 0.8 and tk:
+                tk.append(tk[int(rng.integers(0, len(tk)))])  # a repeated token
+            else:
+                tk.append(int(rng.integers(0, V)))
+        parents += par
+        tokens += tk
+        rows.append(lg)
+    logits = torch.cat(rows).to(dtype).contiguous().cuda()
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
+    T = torch.tensor(rng.choice([0.0, 0.6, 1.0, 1.4], size=B).astype(np.float32)).cuda()
+    w = W.TreeWorkload("random trees", logits, torch.tensor(tokens, dtype=torch.int32).cuda(),
+                       torch.tensor(parents, dtype=torch.int32).cuda(), cu, T, int(rng.integers(0, 2**40)),
+                       [int(c) for c in counts], depth_max)
+    return w, max_nodes, f"B={B} V={V} max_nodes={max_nodes} {str(dtype).split('.')[-1]} depth {depth_max}"
+
+
+@pytest.mark.parametrize("seed", [11, 12])
+def test_random_tree_sweep(seed):
+    import oracle
+    rng = np.random.default_rng(seed)
+    for case in range(12):
+        w, max_nodes, desc = _random_trees(rng)
+        print(f"[gpu-case] tree sweep {seed} case {case}: {desc}", flush=True)
+        max_depth = max(w.max_depth, 1)
+        out, path, n = rs.verify_tree(w.logits, w.node_tokens, w.node_parents, w.cu_num_nodes, w.temperature,
+                                      seed=w.seed, max_nodes=max_nodes, max_depth=max_depth)
+        torch.cuda.synchronize()
+        c = w.to("cpu")
+        o = oracle.verify_tree(c.logits, c.node_tokens, c.node_parents, c.cu_num_nodes, c.temperature, c.seed,
+                               max_nodes, max_depth)
+        ok = ~o.near_tie
+        np.testing.assert_array_equal(n.cpu().numpy()[ok], o.num_accepted[ok], err_msg=desc)
+        np.testing.assert_array_equal(out.cpu().numpy()[ok], o.tokens[ok], err_msg=desc)
+        np.testing.assert_array_equal(path.cpu().numpy()[ok], o.path[ok], err_msg=desc)

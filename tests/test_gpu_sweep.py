@@ -129,3 +129,34 @@ def test_random_tree_sweep(seed):
         np.testing.assert_array_equal(n.cpu().numpy()[ok], o.num_accepted[ok], err_msg=desc)
         np.testing.assert_array_equal(out.cpu().numpy()[ok], o.tokens[ok], err_msg=desc)
         np.testing.assert_array_equal(path.cpu().numpy()[ok], o.path[ok], err_msg=desc)
+
+
+@pytest.mark.parametrize("seed", [21, 22])
+def test_random_ngram_sweep(seed):
+    from oracle import ngram
+    rng = np.random.default_rng(seed)
+    for case in range(15):
+        B = int(rng.integers(1, 200))
+        vocab = int(rng.choice([3, 20, 1000, 151936]))
+        lo = int(rng.integers(0, 50))
+        length = (lo, lo + int(rng.integers(0, 3000)))
+        min_n = int(rng.integers(1, 5))
+        max_n = min_n + int(rng.integers(0, 8))
+        k = int(rng.integers(1, 12))
+        flat, cu = W.make_contexts(B, length, vocab, copy_prob=float(rng.choice([0.0, 0.5, 0.9])),
+                                   seed=int(rng.integers(0, 2**31)), device="cuda")
+        cuh = cu.cpu().numpy()
+        lens = np.diff(cuh)
+        mml = int(rng.choice([1 << 40, int(lens.max()) + int(rng.integers(0, k + 2)) if lens.size else 1]))
+        print(f"[gpu-case] ngram sweep {seed} case {case}: B={B} len={length} vocab={vocab} n={min_n}-{max_n} "
+              f"k={k} max_model_len={mml}", flush=True)
+        d, n, c = rs.ngram_propose(flat, cu, min_n=min_n, max_n=max_n, k=k, max_model_len=mml)
+        torch.cuda.synchronize()
+        f = flat.cpu().numpy()
+        ctxs = [f[cuh[b]:cuh[b + 1]] for b in range(B)]
+        want, wcnt = ngram.propose_batch(ctxs, min_n, max_n, k, mml)
+        n, c, d = n.cpu().numpy(), c.cpu().numpy(), d.cpu().numpy()
+        np.testing.assert_array_equal(n, wcnt)
+        np.testing.assert_array_equal(c, np.concatenate([[0], np.cumsum(wcnt)]))
+        for b in range(B):
+            np.testing.assert_array_equal(d[c[b]:c[b + 1]], want[b, :wcnt[b]])

@@ -12,7 +12,7 @@
 //
 // A filtered row is first streamed by the ordinary row-statistics task, which
 // also stores every thread's maximum of its 16 x 16-byte "segment" of the row
-// (chunk_task's tmax).  filter_kernel then works per row from those maxima:
+// (chunk_task's tmax).  filter_row then works per row from those maxima:
 //   * the k-th largest segment maximum bounds the k-th largest logit from
 //     below (k segments hold an element at least that large); the segment
 //     maxima, taken from the top until their mass reaches the top-p target,
@@ -63,6 +63,26 @@ struct FilterRec {
   double sum;
 };
 static_assert(sizeof(FilterRec) == 16, "FilterRec layout");
+
+// A filter record crosses workgroups inside one kernel (the request's last
+// filter workgroup scans it): agent-scope 64-bit stores and loads, as the
+// other hand-offs, with an s_waitcnt before the arrival is counted.
+__device__ __forceinline__ void store_frec_coherent(FilterRec* p, const FilterRec& f) {
+  unsigned long long* w = reinterpret_cast<unsigned long long*>(p);
+  store_coherent(w, ((unsigned long long)__float_as_uint(f.shift) << 32) | __float_as_uint(f.tau));
+  store_coherent(w + 1, (unsigned long long)__double_as_longlong(f.sum));
+}
+template <bool COH>
+__device__ __forceinline__ FilterRec load_frec(const FilterRec* p) {
+  if (!COH) return *p;
+  const unsigned long long* w = reinterpret_cast<const unsigned long long*>(p);
+  const unsigned long long a = load_coherent(w), b = load_coherent(w + 1);
+  FilterRec f;
+  f.tau = __uint_as_float((uint32_t)a);
+  f.shift = __uint_as_float((uint32_t)(a >> 32));
+  f.sum = __longlong_as_double((long long)b);
+  return f;
+}
 
 // Does request b filter its target distribution?  (Greedy requests ignore it.)
 __device__ __forceinline__ bool filter_on(const int32_t* __restrict__ top_k, const float* __restrict__ top_p,
@@ -625,7 +645,7 @@ __device__ __forceinline__ uint32_t select_list(const float* cand, int n, uint32
 // first phase, still active), after the row task streamed it: writes
 // frec[row] from the row's partials and segment maxima.
 template <typename Elem>
-__global__ __launch_bounds__(kFilterThreads) void filter_kernel(
+__device__ __forceinline__ void filter_row(
     const Elem* __restrict__ logits, const int32_t* __restrict__ cu, const float* __restrict__ temperature,
     const int32_t* __restrict__ top_k, const float* __restrict__ top_p, int32_t D, int32_t max_k, int32_t V,
     int32_t j_begin, int32_t j_count, int32_t nsplit, const ReqRecord* __restrict__ records,
@@ -771,7 +791,8 @@ __global__ __launch_bounds__(kFilterThreads) void filter_kernel(
     f.tau = tau;
     f.shift = shift;
     f.sum = acc;
-    frec[row] = f;
+    store_frec_coherent(frec + row, f);
+    wait_memory();  // acknowledged before thread 0 counts the workgroup's arrival
   }
 }
 

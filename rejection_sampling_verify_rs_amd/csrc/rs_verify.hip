@@ -17,6 +17,10 @@
 //   emit_kernel     one wavefront per random request: chunk winners -> token,
 //                   output row.
 //
+// With top-k / top-p, filter_scan_kernel takes each scan_kernel's place: a
+// workgroup per row of the phase finds the row's threshold and kept mass
+// (filter.hpp), and the last one of each request runs its scan.
+//
 // A request that rejects in phase 1 never has its later rows read: drafts
 // behind a rejected one are discarded [第12章 投机解码：以小博大 §12.9;
 // vllm v1 源码精读（五） §7], so those rows cannot change the output.  One
@@ -79,7 +83,8 @@ __global__ __launch_bounds__(kRowThreads) void phase_kernel(
     int32_t max_k, int32_t V, uint64_t seed, int32_t j_begin, int32_t j_count, int32_t nsplit, int32_t n_row,
     int32_t race_chunks, int32_t n_race, int32_t race_phase, RowPartial* __restrict__ partials,
     Gathered* __restrict__ gath, const ReqRecord* __restrict__ records, unsigned long long* __restrict__ cand,
-    const int32_t* __restrict__ top_k, const float* __restrict__ top_p, float* __restrict__ tmaxbuf) {
+    const int32_t* __restrict__ top_k, const float* __restrict__ top_p, float* __restrict__ tmaxbuf,
+    uint32_t* __restrict__ req_count) {
   const int32_t id = blockIdx.x;
   const int32_t both = min(n_row, n_race);
   int32_t t;
@@ -96,6 +101,8 @@ __global__ __launch_bounds__(kRowThreads) void phase_kernel(
     const int32_t rest = t / nsplit;
     const int32_t j = j_begin + rest % j_count;
     const int32_t b = rest / j_count;
+    // the filter kernel after this one counts its workgroups per request here
+    if (req_count && c == 0 && j == j_begin && threadIdx.x == 0) req_count[b] = 0u;
     const int32_t s = cu[b], e = cu[b + 1];
     if (!request_valid(s, e, D, max_k) || j > e - s) return;
     if (j_begin > 0 && records[b].mode != kModeActive) return;
@@ -130,6 +137,33 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const float* __restrict__ top_p, const FilterRec* __restrict__ frec) {
   scan_phase<Elem>(blockIdx.x, q, draft, cu, temperature, greedy_all, D, max_k, V, nsplit, seed, partials, gath,
                    j_begin, j_end, phase, records, out, num_accepted, dbg_p, top_k, top_p, frec);
+}
+
+// ------------------------------------------------- filter + scan kernel
+// Calls with top-k / top-p: one workgroup per (request, position) row of the
+// phase computes the row's filter record; the last of a request's j_count
+// workgroups to finish then runs the request's scan with its first
+// wavefront (req_count[b], zeroed by the phase's row pass, counts them).
+// Each record is stored agent-coherent and acknowledged before its
+// workgroup arrives; the scan loads the records coherently.
+template <typename Elem>
+__global__ __launch_bounds__(kFilterThreads) void filter_scan_kernel(
+    const Elem* __restrict__ logits, const float* __restrict__ q, const int32_t* __restrict__ draft,
+    const int32_t* __restrict__ cu, const float* __restrict__ temperature, const int32_t* __restrict__ top_k,
+    const float* __restrict__ top_p, int32_t D, int32_t max_k, int32_t V, int32_t j_begin, int32_t j_count,
+    int32_t phase, int32_t nsplit, uint64_t seed, const RowPartial* __restrict__ partials,
+    const Gathered* __restrict__ gath, const float* __restrict__ tmax, ReqRecord* __restrict__ records,
+    FilterRec* __restrict__ frec, uint32_t* __restrict__ req_count, int32_t* __restrict__ out,
+    int32_t* __restrict__ num_accepted, double* __restrict__ dbg_p) {
+  filter_row<Elem>(logits, cu, temperature, top_k, top_p, D, max_k, V, j_begin, j_count, nsplit, records, partials,
+                   tmax, frec);
+  if (threadIdx.x >= 64) return;
+  const int32_t b = (int32_t)(blockIdx.x / j_count);
+  int last = 0;
+  if (threadIdx.x == 0) last = arrive_last(req_count + b, (uint32_t)j_count) ? 1 : 0;
+  if (!__shfl(last, 0)) return;
+  scan_phase<Elem, true>(b, q, draft, cu, temperature, 0, D, max_k, V, nsplit, seed, partials, gath, j_begin,
+                         j_begin + j_count, phase, records, out, num_accepted, dbg_p, top_k, top_p, frec);
 }
 
 // ------------------------------------------------------------- emit kernel
@@ -369,10 +403,10 @@ static void launch_phase(hipStream_t stream, const Elem* logits, const float* q,
                          const int32_t* cu, const float* temperature, int greedy_all, int32_t D, int32_t max_k,
                          int32_t V, uint64_t seed, const PhaseArgs& a, RowPartial* partials, Gathered* gath,
                          const ReqRecord* records, unsigned long long* cand, const int32_t* top_k,
-                         const float* top_p, float* tmax) {
+                         const float* top_p, float* tmax, uint32_t* req_count) {
   phase_kernel<Elem, NV, TPT><<<(unsigned)(a.n_row + a.n_race), kRowThreads, 0, stream>>>(
       logits, q, draft, cu, temperature, greedy_all, D, max_k, V, seed, a.j_begin, a.j_count, a.nsplit, a.n_row,
-      a.race_chunks, a.n_race, a.race_phase, partials, gath, records, cand, top_k, top_p, tmax);
+      a.race_chunks, a.n_race, a.race_phase, partials, gath, records, cand, top_k, top_p, tmax, req_count);
 }
 
 template <typename Elem>
@@ -380,11 +414,11 @@ static bool dispatch_phase(int nv, int tpt, hipStream_t stream, const Elem* logi
                            const int32_t* draft, const int32_t* cu, const float* temperature, int greedy_all,
                            int32_t D, int32_t max_k, int32_t V, uint64_t seed, const PhaseArgs& a,
                            RowPartial* partials, Gathered* gath, const ReqRecord* records, unsigned long long* cand,
-                           const int32_t* top_k, const float* top_p, float* tmax) {
+                           const int32_t* top_k, const float* top_p, float* tmax, uint32_t* req_count) {
 #define RS_PHASE(NV, TPT)                                                                                           \
   if (nv == NV && tpt == TPT) {                                                                                     \
     launch_phase<Elem, NV, TPT>(stream, logits, q, draft, cu, temperature, greedy_all, D, max_k, V, seed, a,        \
-                                partials, gath, records, cand, top_k, top_p, tmax);                                 \
+                                partials, gath, records, cand, top_k, top_p, tmax, req_count);                      \
     return true;                                                                                                    \
   }
   RS_PHASE(16, 32)
@@ -437,6 +471,8 @@ static rs_status launch(const void* logits_v, const float* q, const int32_t* dra
   FilterRec* frec = reinterpret_cast<FilterRec*>(w + p.off_frec);
   float* tmax = reinterpret_cast<float*>(w + p.off_tmax);
   const bool filtered = !greedy_all && (top_k || top_p);
+  // the phased path's per-request filter arrivals reuse the stream path's row counters
+  uint32_t* req_count = filtered ? reinterpret_cast<uint32_t*>(w + p.off_row_count) : nullptr;
   double* dbg_p = dbg ? dbg->draft_target_prob : nullptr;
   EventLog evl{dbg};
   evl.mark(stream);
@@ -499,25 +535,25 @@ static rs_status launch(const void* logits_v, const float* q, const int32_t* dra
       a.race_phase = ph - 1;
       if (!dispatch_phase<Elem>(p.row_nv, p.race_tpt, stream, logits, q, draft, cu, temperature, greedy_all, D,
                                 max_k, V, seed, a, partials, gath, records, cand, top_k, top_p,
-                                filtered ? tmax : nullptr))
+                                filtered ? tmax : nullptr, req_count))
         return RS_ERR_INVALID_ARG;
       if (!evl.after_kernel(stream)) return RS_ERR_HIP;
-      if (filtered) {  // thresholds and kept mass of the filtered requests' rows of this phase
-        filter_kernel<Elem><<<(unsigned)(a.j_count * B), kFilterThreads, 0, stream>>>(
-            logits, cu, temperature, top_k, top_p, D, max_k, V, a.j_begin, a.j_count, p.nsplit, records, partials,
-            tmax, frec);
-        if (!evl.after_kernel(stream)) return RS_ERR_HIP;
+      if (filtered) {  // thresholds and kept mass of this phase's rows, then the scans
+        filter_scan_kernel<Elem><<<(unsigned)(a.j_count * B), kFilterThreads, 0, stream>>>(
+            logits, q, draft, cu, temperature, top_k, top_p, D, max_k, V, a.j_begin, a.j_count, ph, p.nsplit, seed,
+            partials, gath, tmax, records, frec, req_count, out, nacc, dbg_p);
+      } else {
+        scan_kernel<Elem><<<(unsigned)B, kScanThreads, 0, stream>>>(q, draft, cu, temperature, greedy_all, D, max_k,
+                                                                    V, p.nsplit, seed, partials, gath, a.j_begin,
+                                                                    p.bounds[ph], ph, records, out, nacc, dbg_p,
+                                                                    top_k, top_p, frec);
       }
+      if (!evl.after_kernel(stream)) return RS_ERR_HIP;
       if (dbg && dbg->probs && !greedy_all) {
         probs_kernel<Elem><<<(unsigned)((max_k + 1) * B), 256, 0, stream>>>(
             logits, cu, temperature, D, max_k, V, p.nsplit, partials, dbg->probs, top_k, top_p, frec);
         if (!evl.after_kernel(stream)) return RS_ERR_HIP;
       }
-      scan_kernel<Elem><<<(unsigned)B, kScanThreads, 0, stream>>>(q, draft, cu, temperature, greedy_all, D, max_k, V,
-                                                                  p.nsplit, seed, partials, gath, a.j_begin,
-                                                                  p.bounds[ph], ph, records, out, nacc, dbg_p, top_k,
-                                                                  top_p, frec);
-      if (!evl.after_kernel(stream)) return RS_ERR_HIP;
     }
     if (!greedy_all) {  // race of the requests decided in the last phase, then the output rows
       PhaseArgs a;
@@ -529,7 +565,7 @@ static rs_status launch(const void* logits_v, const float* q, const int32_t* dra
       a.n_race = p.race_chunks * B;
       a.race_phase = p.nphases;
       if (!dispatch_phase<Elem>(p.row_nv, p.race_tpt, stream, logits, q, draft, cu, temperature, greedy_all, D,
-                                max_k, V, seed, a, partials, gath, records, cand, top_k, top_p, nullptr))
+                                max_k, V, seed, a, partials, gath, records, cand, top_k, top_p, nullptr, nullptr))
         return RS_ERR_INVALID_ARG;
       if (!evl.after_kernel(stream)) return RS_ERR_HIP;
       emit_kernel<Elem><<<(unsigned)B, 64, 0, stream>>>(logits, draft, max_k, V, p.race_chunks, seed, records, cand,

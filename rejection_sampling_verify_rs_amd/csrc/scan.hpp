@@ -25,7 +25,7 @@
 
 namespace rsv {
 
-template <typename Elem>
+template <typename Elem, bool COH_FREC = false>
 __device__ __forceinline__ void scan_phase(
     int32_t b, const float* __restrict__ q, const int32_t* __restrict__ draft, const int32_t* __restrict__ cu,
     const float* __restrict__ temperature, int32_t greedy_all, int32_t D, int32_t max_k, int32_t V, int32_t nsplit,
@@ -71,7 +71,7 @@ __device__ __forceinline__ void scan_phase(
       const double u = j < K ? accept_uniform(seed, b, j) : 0.0;
       const Gathered g = j < K ? gath[s + j] : Gathered{0.f, 0.f};
       if (filt) {  // p' from the row's filter record; p'(x*) = 0 below the threshold
-        const FilterRec f = frec[row];
+        const FilterRec f = load_frec<COH_FREC>(frec + row);
         shift = f.shift;
         S = f.sum;
         tau = f.tau;

@@ -555,14 +555,63 @@ __device__ __forceinline__ uint32_t select_row(const RowVisitor<Elem>& all, uint
 // select_row).
 constexpr int kValueBins = kFilterThreads / 64 * kStashW;  // 4096: the queues' LDS, as u32 counters
 
-__device__ __forceinline__ uint32_t bf16_key(float l) {  // order key of a widened bf16 value; -0 is +0
-  uint32_t u = __float_as_uint(l) >> 16;
-  u = u == 0x8000u ? 0u : u;
-  return (u & 0x8000u) ? (~u & 0xFFFFu) : (u | 0x8000u);
+// 16-bit order key of a bf16 value u (sign bit, 15-bit magnitude m):
+// 0x8000 + m if positive, 0x8000 - m if negative, so both zeros get 0x8000.
+__device__ __forceinline__ uint32_t bf16_key(float l) {  // l: a widened bf16 value
+  const uint32_t u = __float_as_uint(l) >> 16, m = u & 0x7FFFu;
+  return (u & 0x8000u) ? 0x8000u - m : 0x8000u + m;
 }
 __device__ __forceinline__ float bf16_value(uint32_t key) {
-  const uint32_t u = (key & 0x8000u) ? (key & 0x7FFFu) : (~key & 0xFFFFu);
+  const uint32_t u = key >= 0x8000u ? key - 0x8000u : 0x8000u | (0x8000u - key);
   return __uint_as_float(u << 16);
+}
+
+typedef unsigned short vb_u16x2 __attribute__((ext_vector_type(2)));
+typedef short vb_i16x2 __attribute__((ext_vector_type(2)));
+
+// The distances ktop - key of the two bf16 values packed in w, one per
+// 16-bit half, in packed 16-bit integer arithmetic: with s = 0xFFFF for a
+// negative half, (m ^ s) - s is +m or -m, and ktop - (0x8000 +- m) =
+// (ktop - 0x8000) -+ m modulo 2^16.  top2 holds ktop - 0x8000 in both halves.
+__device__ __forceinline__ uint32_t bf16_pair_dist(uint32_t w, uint32_t top2) {
+  const vb_i16x2 x = __builtin_bit_cast(vb_i16x2, w);
+  const vb_u16x2 s = __builtin_bit_cast(vb_u16x2, (vb_i16x2)(x >> (short)15));
+  const vb_u16x2 m = __builtin_bit_cast(vb_u16x2, w & 0x7FFF7FFFu);
+  const vb_u16x2 d = __builtin_bit_cast(vb_u16x2, top2) - ((m ^ s) - s);
+  return __builtin_bit_cast(uint32_t, d);
+}
+
+// Adds one to cnt[d] for every element of the bf16 row at distance d < dlim
+// below the key ktop, reading the row's 16-byte vectors as 32-bit words.
+__device__ __forceinline__ void count_value_bins(const RowView<uint16_t>& rv, uint32_t ktop, uint32_t dlim,
+                                                 uint32_t* cnt) {
+  constexpr int KB = RowVisitor<uint16_t>::kRowBatch;
+  const uint32_t top2 = ((ktop - 0x8000u) & 0xFFFFu) * 0x10001u;
+  auto pair = [&](uint32_t w) {
+    const uint32_t d = bf16_pair_dist(w, top2);
+    const uint32_t lo = d & 0xFFFFu, hi = d >> 16;
+    if (lo < dlim) atomicAdd(cnt + lo, 1u);
+    if (hi < dlim) atomicAdd(cnt + hi, 1u);
+  };
+  for (int v0 = threadIdx.x; v0 < rv.nvec; v0 += KB * kFilterThreads) {
+    uint4 x[KB];  // unconditional loads (clamped index), all in flight together
+#pragma unroll
+    for (int i = 0; i < KB; ++i) x[i] = rv.pv[min(v0 + i * kFilterThreads, rv.nvec - 1)];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      if (v0 + i * kFilterThreads < rv.nvec) {
+        pair(x[i].x);
+        pair(x[i].y);
+        pair(x[i].z);
+        pair(x[i].w);
+      }
+    }
+  }
+  float e;
+  if (threadIdx.x < 16 && rv.extra(threadIdx.x, e)) {
+    const uint32_t d = ktop - bf16_key(e);
+    if (d < dlim) atomicAdd(cnt + d, 1u);
+  }
 }
 
 template <bool MASS>
@@ -575,16 +624,19 @@ __device__ __forceinline__ uint32_t select_value_bins(const RowVisitor<uint16_t>
   constexpr int PER = kValueBins / kFilterThreads;  // bins per thread: thread t owns [t PER, t PER + PER)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t ktop = bf16_key(rowmax);
+  // l >= lo_pre  <=>  bf16_key(l) >= klo, the key of the least bf16 value >= lo_pre
+  // (bf16_key truncates lo_pre towards zero)
+  uint32_t klo = 0u;
+  if (lo_pre > -INFINITY) {
+    klo = bf16_key(lo_pre);
+    if (bf16_value(klo) < lo_pre) ++klo;
+  }
+  const uint32_t dlim = klo > ktop ? 0u : min(ktop - klo + 1u, (uint32_t)kValueBins);  // bin 0 = the maximum
   __syncthreads();  // earlier users of the LDS are done
   for (int i = tid; i < kValueBins; i += kFilterThreads) cnt[i] = 0u;
   if (tid == 0) *s_bin = -1;
   __syncthreads();
-  all([&](float l) {
-    if (l >= lo_pre) {
-      const uint32_t d = ktop - bf16_key(l);  // bin 0 = the maximum (no key exceeds ktop)
-      if (d < (uint32_t)kValueBins) atomicAdd(cnt + d, 1u);
-    }
-  });
+  count_value_bins(all.rv, ktop, dlim, cnt);
   __syncthreads();
   unsigned long long w[PER], sum = 0ull;
 #pragma unroll

@@ -153,7 +153,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", type=int, default=4, help="1..5 (4 = B=256 K=8 V=151936)")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget (0 = skip)")

@@ -720,14 +720,14 @@ rs_status rs_verify_tree(const void* target_logits, rs_dtype logits_dtype, const
                                                                   output_token_ids, num_accepted)
   if (logits_dtype == RS_BF16) {
     if (big)
-      RS_TREE(uint16_t, 1024);
+      RS_TREE(uint16_t, 512);
     else
       RS_TREE(uint16_t, 256);
     if (hipGetLastError() != hipSuccess) return RS_ERR_HIP;
     RS_TREE_RACE(uint16_t);
   } else {
     if (big)
-      RS_TREE(float, 1024);
+      RS_TREE(float, 512);
     else
       RS_TREE(float, 256);
     if (hipGetLastError() != hipSuccess) return RS_ERR_HIP;

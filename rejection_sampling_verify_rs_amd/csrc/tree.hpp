@@ -50,7 +50,8 @@ __global__ __launch_bounds__(NT) void tree_kernel(
     int32_t max_depth, int32_t V, uint64_t seed, int32_t* __restrict__ out, int32_t* __restrict__ path,
     int32_t* __restrict__ num_accepted, ReqRecord* __restrict__ records) {
   constexpr int NW = NT / 64;
-  constexpr int NVP = NT >= 1024 ? 4 : 16;  // 16-byte vectors per thread per statistics pass (no spills)
+  // 16-byte vectors per thread per statistics pass (the most without spills)
+  constexpr int NVP = NT >= 1024 ? 4 : (NT >= 512 ? 8 : 16);
   __shared__ float s_f[NW];
   __shared__ int s_i[NW];
   __shared__ double s_d[NW];

@@ -54,6 +54,10 @@ constexpr int kHistStride = kFilterBins + 1;
 constexpr int kFilterCand = 4096;     // candidate list entries in LDS
 constexpr int kStashW = 1024;         // per-wavefront LDS queue of window elements (select_row)
 constexpr int kFilterSegList = 1024;  // segments re-read per row at most
+// With bf16 logits a bound that admits more segments than this skips the
+// gather for the one-pass value-bin selection over the row: ~1000 listed
+// segments took ~55 us to gather against ~28 us for the value bins.
+constexpr int kGatherMaxSegsBf16 = 384;
 constexpr int kSegVectors = 16;       // 16-byte vectors per segment: the row task's vectors per thread
 
 // Per-row result: keep l >= tau; shift = fl32(max * c); sum = S' (fp64).
@@ -364,11 +368,12 @@ __device__ __forceinline__ unsigned long long fixed_total(const Vis& vis, uint32
 // chunk sg / 256, thread sg % 256, holding vectors chunk * 4096 + thread +
 // u * 256 for u < 16, plus a head / tail element in chunk 0).  The segments
 // are listed first, then all threads share their (segment, vector) loads.
-// Returns the element count, or -1 if the segments or the elements overflow
-// their lists.
+// Returns the element count, or -1 if more than max_segs segments qualify or
+// the elements overflow their list.
 template <typename Elem>
 __device__ __forceinline__ int gather_segments(const RowView<Elem>& rv, const float (&mx)[kSegPerThread], float t,
-                                               float* cand, int* qseg, int* s_cnt, int* s_nq) {
+                                               float* cand, int* qseg, int* s_cnt, int* s_nq,
+                                               int max_segs = kFilterSegList) {
   using VT = Vec<Elem>;
   constexpr int kItems = kSegVectors + 1;  // 16 vectors and the head / tail element
   constexpr int kBatch = 4;
@@ -388,7 +393,7 @@ __device__ __forceinline__ int gather_segments(const RowView<Elem>& rv, const fl
   }
   __syncthreads();
   const int nq = *s_nq;
-  if (nq > kFilterSegList || rv.nvec == 0) return -1;  // (rows shorter than one vector: whole-row selection)
+  if (nq > max_segs || rv.nvec == 0) return -1;  // (rows shorter than one vector: whole-row selection)
   auto put = [&](float l) {
     if (l >= t) {
       const int slot = atomicAdd(s_cnt, 1);
@@ -737,6 +742,7 @@ __device__ __forceinline__ void filter_row(
     mx[i] = (use_maxima && sg < nseg) ? v : -INFINITY;
   }
   const MaxVisitor maxima{mx};
+  const int max_segs = sizeof(Elem) == 2 ? kGatherMaxSegsBf16 : kFilterSegList;  // beyond: the value bins
   constexpr int kBoundLevels = 2;  // key bits that bound a threshold from the maxima
 
   float shift;
@@ -760,7 +766,7 @@ __device__ __forceinline__ void filter_row(
         use_maxima
             ? radix_select<Elem, false>(maxima, 0u, (double)kb, cs, shift, kBoundLevels, hist, s_u64, &s_bin)
             : 0u;
-    if (bound) ncand = gather_segments(rv, mx, key_value(bound), cand, qseg, &s_cnt, &s_nq);
+    if (bound) ncand = gather_segments(rv, mx, key_value(bound), cand, qseg, &s_cnt, &s_nq, max_segs);
     if (ncand >= 0) {
       kappa = select_list<Elem, false>(cand, ncand, 0u, (double)kb, cs, shift, hist, wts, s_u64, &s_bin, &s_key);
     } else {
@@ -789,7 +795,7 @@ __device__ __forceinline__ void filter_row(
       const uint32_t bound =
           use_maxima ? radix_select<Elem, true>(maxima, kappa, P, cs, shift, kBoundLevels, hist, s_u64, &s_bin)
                      : 0u;
-      if (bound) ncand = gather_segments(rv, mx, key_value(bound), cand, qseg, &s_cnt, &s_nq);
+      if (bound) ncand = gather_segments(rv, mx, key_value(bound), cand, qseg, &s_cnt, &s_nq, max_segs);
     }
     uint32_t kp;
     if (ncand >= 0) {

@@ -88,9 +88,19 @@ def compare(g: GpuResult, o: oracle.OracleResult, w: W.Workload, *, max_flag_fra
     return {"requests": int(flagged.size), "flagged": int(flagged.sum()), "flag_frac": frac}
 
 
-def compare_p(g: GpuResult, o: oracle.OracleResult) -> float:
-    """p(x*) at every position the oracle evaluated, within P_RTOL relative.  Returns the max rel error."""
+def compare_p(g: GpuResult, o: oracle.OracleResult, w: Optional[W.Workload] = None) -> float:
+    """p(x*) at every position the oracle evaluated, within P_RTOL relative.  Returns the max rel error.
+
+    With the workload w, positions of requests whose top-p boundary is a near
+    tie (FLAG_TOPP_TIE: the cumulative mass just above the boundary value lies
+    within the tie margin of top_p times the mass) are left out: the kept set,
+    and with it S' and p'(x*), then has two valid values, like the tokens of
+    any flagged request."""
     have = ~np.isnan(o.p_draft)
+    if w is not None:
+        cu = w.cu_num_draft_tokens.cpu().numpy().astype(np.int64)
+        slot_req = np.repeat(np.arange(cu.size - 1), np.diff(cu))
+        have &= ((o.flags & oracle.FLAG_TOPP_TIE) == 0)[slot_req]
     if not have.any():
         return 0.0
     pg, po = g.p_draft[have], o.p_draft[have]

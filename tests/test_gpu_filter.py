@@ -80,7 +80,7 @@ def test_filtered_parity(name, build):
     g = run_gpu(w, want_p=True)
     o = run_oracle(w)
     rep = compare(g, o, w)
-    worst = compare_p(g, o)
+    worst = compare_p(g, o, w)
     _say(f"{name}: flagged {rep['flagged']}/{rep['requests']}, max p' rel err {worst:.3e}")
     assert rep["flagged"] <= MAX_FLAGGED.get(name, 1)
 
@@ -92,7 +92,7 @@ def test_workload_with_filters(n):
     g = run_gpu(w, want_p=True)
     o = run_oracle(w)
     rep = compare(g, o, w)
-    worst = compare_p(g, o)
+    worst = compare_p(g, o, w)
     _say(f"workload {n} filtered: flagged {rep['flagged']}/{rep['requests']}, max p' rel err {worst:.3e}, "
          f"mean accepted {o.num_accepted.mean():.3f}")
     assert rep["flagged"] <= 1
@@ -108,7 +108,7 @@ def test_top_p_alone_full_size(n, tp):
     g = run_gpu(w, want_p=True)
     o = run_oracle(w)
     rep = compare(g, o, w)
-    worst = compare_p(g, o)
+    worst = compare_p(g, o, w)
     _say(f"workload {n} top_p {tp}: flagged {rep['flagged']}/{rep['requests']}, max p' rel err {worst:.3e}")
     assert rep["flagged"] <= 2
 
@@ -178,7 +178,7 @@ def test_signed_zeros_at_threshold():
     for _ in range(3):  # ties of equal values once raced here: repeat
         g = run_gpu(w, want_p=True)
         rep = compare(g, o, w)
-        compare_p(g, o)
+        compare_p(g, o, w)
         assert rep["flagged"] == 0
 
 

@@ -38,7 +38,7 @@ def test_workload_full_size(n):
     g = run_gpu(w, want_p=True)
     o = run_oracle(w)
     rep = compare(g, o, w)
-    worst = compare_p(g, o)
+    worst = compare_p(g, o, w)
     _say(f"workload {n}: flagged {rep['flagged']}/{rep['requests']}, max p rel err {worst:.3e}, "
          f"mean accepted {o.num_accepted.mean():.3f}")
     assert rep["flagged"] <= 1
@@ -84,7 +84,7 @@ def test_small_ragged(case):
     g = run_gpu(w, want_p=True)
     o = run_oracle(w)
     compare(g, o, w)
-    compare_p(g, o)
+    compare_p(g, o, w)
 
 
 def test_full_probs_small():
@@ -125,7 +125,7 @@ def test_paths_and_phases_full_size(n, path, phases):
     g = run_gpu(w, path=path, phases=phases, want_p=True)
     o = run_oracle(w)
     compare(g, o, w)
-    compare_p(g, o)
+    compare_p(g, o, w)
 
 
 @pytest.mark.parametrize("ks,V,want", [([4], 1024, 1), ([5] * 8, 1024, 1), ([4] * 16, 32000, 3), ([8] * 32, 151936, 3),
@@ -200,7 +200,7 @@ def test_tiny_temperature():
     _say("T = 0.01")
     g, o = run_gpu(w, want_p=True), run_oracle(w)
     compare(g, o, w)
-    compare_p(g, o)
+    compare_p(g, o, w)
 
 
 def test_q_zero_at_draft_accepts():

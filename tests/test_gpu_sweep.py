@@ -67,7 +67,7 @@ def test_random_parity_sweep(seed):
         g = run_gpu(w, want_p=True)
         o = run_oracle(w)
         compare(g, o, w)
-        compare_p(g, o)
+        compare_p(g, o, w)
 
 
 def _random_trees(rng):

@@ -14,15 +14,15 @@
  *    p = softmax(l / T), applied to the target only.
  *      [Ch.12 "投机解码：以小博大" §12.2.3; §12.9, compute_probs bullet]
  *  - Accept test at each draft position j, in order: draw u ~ U[0,1) and
- *    accept the draft token x* iff u * q(x*) < p(x*), which is the rule
- *    "accept with probability min(1, p(x*)/q(x*))".
+ *    accept the draft token x* iff u * q(x*) < p(x*), which accepts with
+ *    probability min(1, p(x*)/q(x*)).
  *      [Ch.12 §12.2.1 steps 1-3; "投机解码（Speculative Decoding）端到端深挖"
  *       §7.3 path C (coin * q < p)]
  *    With no draft probabilities the draft is deterministic and q is one-hot
  *    at x*, so q(x*) = 1.  [Ch.12 §12.2.3; §12.9, last bullet]
  *  - First-rejection prefix: drafts after the first rejected one are
- *    discarded.  [Ch.12 §12.9, "one program per request checks its k drafts
- *    in order"; "vllm v1 源码精读（五）" §7]
+ *    discarded.  [Ch.12 §12.9 (each request's drafts are checked in order by
+ *    one program); "vllm v1 源码精读（五）" §7]
  *  - At the first rejected position j = n < K: resample from the residual
  *    max(0, p - q) / sum max(0, p - q)  [Ch.12 §12.2.1 step 3, §12.2.2];
  *    with one-hot q this is p with p(x*) set to zero, renormalised

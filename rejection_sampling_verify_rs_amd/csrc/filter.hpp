@@ -30,7 +30,8 @@
 //     deterministic;
 //   * S' is summed over the list.
 // When no bound can be formed (k above the number of segments, segment maxima
-// lighter than the top-p target) or the list overflows, the selection runs
+// lighter than the top-p target), the bound admits too many segments (with
+// bf16 logits: more than kGatherMaxSegsBf16) or the list overflows, the selection runs
 // over the whole row, re-read from memory: for bf16 logits by exact value
 // (select_value_bins), else -- or when the threshold lies below the values
 // that method counts -- by distance bins (select_row).

@@ -1,8 +1,19 @@
 // rs_verify.hip -- gfx950 kernels and C ABI of the batched speculative-
 // sampling verify step (see include/rs_verify.h for the contract).
 //
-// Default (phased) path.  Draft positions are processed breadth-first in
-// phases, every kernel spreading its work over the whole GPU:
+// Three paths compute the same outputs; make_plan picks one per call (the
+// caller can force one through rs_debug):
+//
+//  * stream (stream_path.hpp): one kernel streams every row position-major in
+//    V-chunks, takes each request's decision in the kernel as its rows
+//    complete, and races decided requests' rows in the same grid; an init
+//    kernel before it and a race tail kernel after it.  Chosen for large
+//    batches and for calls of up to 128 MB of logits.
+//  * per-request (request_path.hpp): one workgroup per request walks its rows
+//    in order and races its row.  Chosen for a few short requests.
+//  * phased (here): draft positions breadth-first in phases, every kernel
+//    spreading its work over the whole GPU.  Chosen otherwise, and for every
+//    call with top-k / top-p:
 //
 //   phase_kernel 1  row statistics of positions [0, P1) of every request, one
 //                   workgroup per (row, V-chunk) (row_pass.hpp).
@@ -17,15 +28,13 @@
 //   emit_kernel     one wavefront per random request: chunk winners -> token,
 //                   output row.
 //
-// With top-k / top-p, filter_scan_kernel takes each scan_kernel's place: a
-// workgroup per row of the phase finds the row's threshold and kept mass
-// (filter.hpp), and the last one of each request runs its scan.
+//   With top-k / top-p, filter_scan_kernel takes each scan_kernel's place: a
+//   workgroup per row of the phase finds the row's threshold and kept mass
+//   (filter.hpp), and the last one of each request runs its scan.
 //
-// A request that rejects in phase 1 never has its later rows read: drafts
-// behind a rejected one are discarded [第12章 投机解码：以小博大 §12.9;
-// vllm v1 源码精读（五） §7], so those rows cannot change the output.  One
-// phase reads every row.  The per-request path (request_path.hpp) is the
-// alternative selected through rs_debug.
+// No path reads the rows behind a request's first rejection: drafts behind a
+// rejected one are discarded [第12章 投机解码：以小博大 §12.9; vllm v1 源码精读（五）
+// §7], so those rows cannot change the output (one phase reads every row).
 //
 // All accesses are bounded by the host-checked sizes; requests with
 // out-of-range metadata are written as invalid instead of being read.

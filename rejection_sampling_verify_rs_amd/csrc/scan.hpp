@@ -9,8 +9,10 @@
 //  - the first rejected position n ends the request: later drafts are
 //    discarded [§12.9; vllm v1 源码精读（五） §7]; a ballot finds it.
 //  - a request with top-k / top-p takes shift, sum and the threshold tau of
-//    each row from the filter kernel's record: p'(x*) = 0 when l(x*) < tau
-//    [§12.2.3; §12.9 (compute_probs)].
+//    each row from the filter's record: p'(x*) = 0 when l(x*) < tau
+//    [§12.2.3; §12.9 (compute_probs)].  COH_FREC: the records were written by
+//    other workgroups of the same kernel (the fused filter + scan kernel) and
+//    are read with agent-coherent loads.
 //  - if no position of the phase rejects and the bonus row K lies in it,
 //    n = K (bonus) [§12.3.2]; otherwise the request stays active for the
 //    next phase.

@@ -83,6 +83,14 @@
  *                 kept tokens is within eps * top_p * S_k of top_p * S_k
  *                 (S_k = the top-k-filtered mass) on a sampled or tested row.
  *
+ * Parity unpinned: the specific token ids drawn at a given seed (the race
+ * winners and the accept coins) are fixed by nothing on the pages, which name
+ * no generator.  The laws they follow are pinned (the output marginal equals
+ * p, the acceptance rate, the expected accept length, greedy brute force), and
+ * the stream itself only by its published definition: this Philox4x32-10
+ * against the Random123 known-answer tests and rocRAND, and a second,
+ * independent implementation on the HIP side.
+ *
  * Arithmetic: inputs are widened exactly (bf16 -> fp32 -> fp64; temperature
  * from fp32) and everything is computed in fp64 with the C library's exp/log.
  * Requests are independent; OpenMP runs them in parallel without changing

@@ -327,8 +327,10 @@ def main():
                         ("one_phase_every_row", {"sampling_path": 2, "phase_ends": (-1,)}),
                         ("per_request", {"sampling_path": 1})):
         ms_v = timed_steps(**knobs)
-        variants[name] = {"ms_per_step": ms_v, "positions_per_s": w0.D / (ms_v / 1e3)}
-        log(f"{name}: {ms_v * 1e3:.1f} us/step, {w0.D / (ms_v / 1e3):.3g} positions/s")
+        variants[name] = {"ms_per_step": ms_v, "positions_per_s": w0.D / (ms_v / 1e3),
+                          "algorithmic_GBps": alg_every / (ms_v / 1e3) / 1e9}
+        log(f"{name}: {ms_v * 1e3:.1f} us/step, {w0.D / (ms_v / 1e3):.3g} positions/s, "
+            f"{variants[name]['algorithmic_GBps'] / HBM_PEAK_GBPS:.1%} of the HBM roofline on algorithmic bytes")
     if args.sweep:
         for split in ((1,), (2,), (3,), (4,), (5,), (1, 3), (2, 4), (2, 5), (3, 5), (1, 2, 4), (1, 3, 5), (2, 3, 5)):
             ms_v = timed_steps(phase_ends=split)
@@ -344,9 +346,11 @@ def main():
         ms_v = timed_steps()
         tk = kernel_times()
         variants[name] = {"ms_per_step": ms_v, "positions_per_s": w0.D / (ms_v / 1e3),
+                          "algorithmic_GBps": alg_every / (ms_v / 1e3) / 1e9,
                           "kernel_us": [round(x * 1e3, 1) for x in tk]}
-        log(f"{name}: {ms_v * 1e3:.1f} us/step, {w0.D / (ms_v / 1e3):.3g} positions/s; kernels (us) "
-            f"{variants[name]['kernel_us']}")
+        log(f"{name}: {ms_v * 1e3:.1f} us/step, {w0.D / (ms_v / 1e3):.3g} positions/s, "
+            f"{variants[name]['algorithmic_GBps'] / HBM_PEAK_GBPS:.1%} of the HBM roofline on algorithmic bytes; "
+            f"kernels (us) {variants[name]['kernel_us']}")
     filt["top_k"] = filt["top_p"] = None
     for i in range(args.copies):  # the unfiltered outcome of every copy again
         call(i)

@@ -20,6 +20,7 @@ namespace rsv {
 
 constexpr int kNgramThreads = 256;
 constexpr int kNgramMaxN = 64;
+constexpr int kNgramBatch = 16;  // context positions per thread whose tokens are loaded together
 
 __global__ __launch_bounds__(kNgramThreads) void ngram_kernel(const int32_t* __restrict__ ctx,
                                                              const int32_t* __restrict__ cu, int32_t total,
@@ -45,13 +46,29 @@ __global__ __launch_bounds__(kNgramThreads) void ngram_kernel(const int32_t* __r
   if (tid < max_n) s_tail[tid] = tid < N ? c[N - 1 - tid] : -1;
   if (tid <= max_n) s_best[tid] = INT_MAX;
   __syncthreads();
-  // end positions e in [min_n - 1, N - min_n - 1]
-  for (int32_t pos = min_n - 1 + tid; pos <= N - min_n - 1; pos += kNgramThreads) {
-    int32_t sl = 0;
-    while (sl < max_n && pos - sl >= 0 && c[pos - sl] == s_tail[sl]) ++sl;
-    // n-grams of every length n <= sl end at pos; each also needs pos <= N - n - 1
-    const int32_t top = min(sl, N - 1 - pos);
-    for (int32_t n = min_n; n <= top; ++n) atomicMin(s_best + n, pos);
+  // End positions e in [min_n - 1, N - min_n - 1].  The token at each of a
+  // thread's kNgramBatch positions is loaded first, all in flight together;
+  // only a position whose token equals the context's last one reads further
+  // back (a chain of dependent loads per position was the kernel's latency).
+  const int32_t last_pos = N - min_n - 1;
+  const int32_t t0 = s_tail[0];
+  for (int32_t base = min_n - 1 + tid; base <= last_pos; base += kNgramThreads * kNgramBatch) {
+    int32_t tok[kNgramBatch];
+#pragma unroll
+    for (int i = 0; i < kNgramBatch; ++i) {
+      const int32_t pos = base + i * kNgramThreads;
+      tok[i] = pos <= last_pos ? c[pos] : ~t0;
+    }
+#pragma unroll
+    for (int i = 0; i < kNgramBatch; ++i) {
+      const int32_t pos = base + i * kNgramThreads;
+      if (pos > last_pos || tok[i] != t0) continue;
+      int32_t sl = 1;
+      while (sl < max_n && pos - sl >= 0 && c[pos - sl] == s_tail[sl]) ++sl;
+      // n-grams of every length n <= sl end at pos; each also needs pos <= N - n - 1
+      const int32_t top = min(sl, N - 1 - pos);
+      for (int32_t n = min_n; n <= top; ++n) atomicMin(s_best + n, pos);
+    }
   }
   __syncthreads();
   if (tid == 0) {

@@ -30,7 +30,12 @@ FLAG_RACE_TIE = 2
 FLAG_ZERO_RESIDUAL = 4
 FLAG_INVALID = 8
 FLAG_TOPP_TIE = 16
-NEAR_TIE_FLAGS = FLAG_ACCEPT_TIE | FLAG_RACE_TIE | FLAG_ZERO_RESIDUAL | FLAG_TOPP_TIE
+FLAG_CAND_OVERFLOW = 32
+# A zero residual (FLAG_ZERO_RESIDUAL) is an exact decision: the oracle adds
+# FLAG_RACE_TIE when the perturbation could flip it.
+NEAR_TIE_FLAGS = FLAG_ACCEPT_TIE | FLAG_RACE_TIE | FLAG_TOPP_TIE
+# near-tied race alternatives reported per request (the winner first, -1 padded)
+NCAND = 8
 
 DEFAULT_EPS = 1e-6
 
@@ -56,14 +61,14 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
     i32, i64, u64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_double
-    lib.rso_verify.argtypes = [P, i32, P, P, P, P, i32, i32, i32, i32, u64, i32, f64, P, P, P, P, i32]
+    lib.rso_verify.argtypes = [P, i32, P, P, P, P, i32, i32, i32, i32, u64, i32, f64, P, P, P, P, P, i32]
     lib.rso_verify.restype = ctypes.c_int
     lib.rso_verify_filtered.argtypes = [P, i32, P, P, P, P, P, P, i32, i32, i32, i32, u64, i32, f64, P, P, P, P,
-                                        i32]
+                                        P, i32]
     lib.rso_verify_filtered.restype = ctypes.c_int
     lib.rso_filtered_probs_row.argtypes = [P, i32, f64, i32, f64, f64, P, P, P]
     lib.rso_filtered_probs_row.restype = None
-    lib.rso_verify_tree.argtypes = [P, i32, P, P, P, P, i32, i32, i32, i32, i32, u64, f64, P, P, P, P, i32]
+    lib.rso_verify_tree.argtypes = [P, i32, P, P, P, P, i32, i32, i32, i32, i32, u64, f64, P, P, P, P, P, i32]
     lib.rso_verify_tree.restype = ctypes.c_int
     lib.rso_probs.argtypes = [P, i32, P, P, i32, i32, P]
     lib.rso_probs.restype = ctypes.c_int
@@ -116,6 +121,7 @@ class OracleResult:
     num_accepted: np.ndarray  # [B] int32
     flags: np.ndarray         # [B] int32, FLAG_* bits
     p_draft: np.ndarray       # [D] float64, p(x*) where evaluated, NaN elsewhere
+    cand: np.ndarray          # [B, NCAND] int32: the race winner, then its near-tied alternatives, -1 padded
 
     @property
     def near_tie(self) -> np.ndarray:
@@ -149,12 +155,13 @@ def verify(logits, draft_probs, draft_token_ids, cu_num_draft_tokens, temperatur
     nacc = np.empty(B, np.int32)
     flags = np.empty(B, np.int32)
     pd = np.empty(D, np.float64)
+    cand = np.empty((B, NCAND), np.int32)
     rc = lib.rso_verify_filtered(_ptr(lg), code, _ptr(q), _ptr(ids), _ptr(cu), _ptr(T), _ptr(tk), _ptr(tp),
                                  B, D, max_k, V, int(seed) & ((1 << 64) - 1), int(greedy_only), float(eps),
-                                 _ptr(out), _ptr(nacc), _ptr(flags), _ptr(pd), int(threads))
+                                 _ptr(out), _ptr(nacc), _ptr(flags), _ptr(pd), _ptr(cand), int(threads))
     if rc != 0:
         raise RuntimeError("oracle rejected its arguments")
-    return OracleResult(out, nacc, flags, pd)
+    return OracleResult(out, nacc, flags, pd, cand)
 
 
 @dataclass
@@ -163,6 +170,7 @@ class TreeResult:
     path: np.ndarray          # [B, max_depth] accepted node indices (request-local), -1 padded
     num_accepted: np.ndarray  # [B] int32
     flags: np.ndarray         # [B] int32
+    cand: np.ndarray          # [B, NCAND] int32: the stop race's winner, then near-tied alternatives
 
     @property
     def near_tie(self) -> np.ndarray:
@@ -188,12 +196,13 @@ def verify_tree(logits, node_tokens, node_parents, cu_num_nodes, temperature, se
     path = np.empty((B, max(max_depth, 0)), np.int32)
     nacc = np.empty(B, np.int32)
     flags = np.empty(B, np.int32)
+    cand = np.empty((B, NCAND), np.int32)
     rc = lib.rso_verify_tree(_ptr(lg), code, _ptr(tok), _ptr(par), _ptr(cu), _ptr(T), B, N, int(max_nodes),
                              int(max_depth), V, int(seed) & ((1 << 64) - 1), float(eps), _ptr(out), _ptr(path),
-                             _ptr(nacc), _ptr(flags), int(threads))
+                             _ptr(nacc), _ptr(flags), _ptr(cand), int(threads))
     if rc != 0:
         raise RuntimeError("oracle rejected its arguments")
-    return TreeResult(out, path, nacc, flags)
+    return TreeResult(out, path, nacc, flags, cand)
 
 
 def verify_greedy(logits, draft_token_ids, cu_num_draft_tokens, max_k: int,

@@ -67,8 +67,14 @@
  *      race exponential E_x = -ln U_x, U_x = ((w >> 9) + 1/2) * 2^-23,
  *        counter (x >> 2, j, b, 1), word (x & 3).
  *  - Greedy and race ties: lowest token index wins.
- *  - All-zero residual after a rejection (possible only through rounding):
- *    race over p at that position instead, and flag the request.
+ *  - All-zero residual after a rejection: max(0, p - q) / sum is undefined
+ *    when p <= q everywhere [Ch.12 §12.2.1 step 3 normalises by that sum].
+ *    With normalised q this happens only through rounding; with q that is
+ *    not normalised (q >= p everywhere, e.g. q = 2p) it happens at every
+ *    rejection.  Reading: race over p at that position instead
+ *    (FLAG_ZERO_RESIDUAL).  This is an ordinary, exactly reproducible
+ *    decision, not a near tie, unless the eps perturbation below could make
+ *    the residual positive.
  *  - Requests whose metadata is out of range (cu not within [0, D], K_b >
  *    max_k, a draft id outside [0, V)) emit -1 everywhere and
  *    num_accepted = -1.
@@ -78,7 +84,13 @@
  *   accept test:  |p(x*) - u q(x*)| <= eps * p(x*)
  *   race:         lower bound of the winner's key <= upper bound of any
  *                 other key, the bounds taken with p -> p(1 -/+ eps) and
- *                 E -> E(1 +/- eps).
+ *                 E -> E(1 +/- eps); or the choice between the residual race
+ *                 and the zero-residual fallback could flip (some upper
+ *                 residual bound positive although every residual is zero,
+ *                 or the winner's lower residual bound zero).
+ *   The near-tied alternatives of the race are reported per request (the
+ *   winner first), so a flagged request can still be checked for a valid
+ *   token.
  *   top-p:        for some group of equal logits, the mass of the larger
  *                 kept tokens is within eps * top_p * S_k of top_p * S_k
  *                 (S_k = the top-k-filtered mass) on a sampled or tested row.
@@ -112,6 +124,7 @@
 #define RSO_FLAG_ZERO_RESIDUAL 4
 #define RSO_FLAG_INVALID 8
 #define RSO_FLAG_TOPP_TIE 16
+#define RSO_FLAG_CAND_OVERFLOW 32
 
 /* ------------------------------------------------------------------------ */
 /* Philox4x32-10.  One round maps (c0, c1, c2, c3) with key (k0, k1) to
@@ -278,9 +291,13 @@ static void load_row(const void* logits, int dtype, int64_t row, int32_t V, doub
 /* Exponential race over r (r[x] > 0 are the candidates).  Returns the winner
  * (lowest index among equal keys) or -1 when every r[x] is zero.  *near_tie is
  * set if the winner's key taken with (rlo, E(1+eps)) does not exceed some
- * other token's key taken with (rhi, E(1-eps)).  E is scratch of length V. */
+ * other token's key taken with (rhi, E(1-eps)).  cand (RSO_NCAND entries, or NULL) receives
+ * the winner, then the tokens whose upper key reaches the winner's lower key,
+ * -1 padded; *overflow is set when they do not all fit.  E is scratch of
+ * length V. */
+#define RSO_NCAND 8
 static int32_t race(const double* r, const double* rlo, const double* rhi, int32_t V, uint64_t seed,
-                    int32_t b, int32_t j, double eps, double* E, int* near_tie) {
+                    int32_t b, int32_t j, double eps, double* E, int* near_tie, int32_t* cand, int* overflow) {
   int32_t win = -1;
   double best = 0.0;
   for (int32_t x = 0; x < V; ++x) {
@@ -293,17 +310,93 @@ static int32_t race(const double* r, const double* rlo, const double* rhi, int32
     }
   }
   *near_tie = 0;
+  *overflow = 0;
+  if (cand)
+    for (int i = 0; i < RSO_NCAND; ++i) cand[i] = -1;
   if (win < 0) return -1;
+  int nc = 0;
+  if (cand) cand[nc++] = win;
   double lo = rlo[win] / (E[win] * (1.0 + eps));
   for (int32_t x = 0; x < V; ++x) {
     if (x == win || !(rhi[x] > 0.0)) continue;
     double hi = rhi[x] / (E[x] * (1.0 - eps));
     if (hi >= lo) {
       *near_tie = 1;
-      break;
+      if (cand && nc < RSO_NCAND)
+        cand[nc++] = x;
+      else
+        *overflow = 1;
     }
   }
   return win;
+}
+
+/* Appends token x to a -1 padded candidate list unless present; sets
+ * *overflow when the list is full. */
+static void cand_add(int32_t* cand, int32_t x, int* overflow) {
+  if (!cand || x < 0) return;
+  for (int i = 0; i < RSO_NCAND; ++i) {
+    if (cand[i] == x) return;
+    if (cand[i] < 0) {
+      cand[i] = x;
+      return;
+    }
+  }
+  *overflow = 1;
+}
+
+/* The sampling race of one request at position n over r, with the
+ * all-zero-residual fallback: when every r(x) is zero, race over p at the same
+ * position instead (flag FLAG_ZERO_RESIDUAL).  The choice between the two
+ * races is itself a decision; it is a near tie (FLAG_RACE_TIE) when the eps
+ * perturbation could flip it:
+ *   - the fallback was taken but some rhi(x) > 0: a perturbed residual would
+ *     race over those tokens, which join the candidates;
+ *   - the residual race was taken but its winner's rlo is 0: a perturbed
+ *     residual could be all zero, so the fallback's candidates join.
+ * cand (RSO_NCAND entries or NULL) receives the winner first, then every
+ * near-tied alternative; FLAG_CAND_OVERFLOW marks a list that did not fit.
+ * r, rlo and rhi are overwritten. */
+static int32_t sample_with_fallback(double* r, double* rlo, double* rhi, const double* p, int32_t V,
+                                    uint64_t seed, int32_t b, int32_t n, double eps, double* E, int32_t* flags,
+                                    int32_t* cand) {
+  int tie = 0, over = 0;
+  int32_t token = race(r, rlo, rhi, V, seed, b, n, eps, E, &tie, cand, &over);
+  int fallback_fragile = 0;
+  int32_t alt[RSO_NCAND];
+  int n_alt = 0;
+  if (token < 0) {
+    *flags |= RSO_FLAG_ZERO_RESIDUAL;
+    for (int32_t x = 0; x < V; ++x)
+      if (rhi[x] > 0.0) {
+        fallback_fragile = 1;
+        if (n_alt < RSO_NCAND) alt[n_alt++] = x;
+        else over = 1;
+      }
+  }
+  const int winner_fragile = token >= 0 && !(rlo[token] > 0.0);
+  if (token < 0 || winner_fragile) {
+    for (int32_t x = 0; x < V; ++x) {
+      r[x] = p[x];
+      rlo[x] = p[x] * (1.0 - eps);
+      rhi[x] = p[x] * (1.0 + eps);
+    }
+    int tie2 = 0, over2 = 0;
+    int32_t fb_cand[RSO_NCAND];
+    int32_t fb = race(r, rlo, rhi, V, seed, b, n, eps, E, &tie2, fb_cand, &over2);
+    if (token < 0) {
+      token = fb;
+      tie |= tie2;
+      if (cand) memcpy(cand, fb_cand, sizeof fb_cand);
+    } else {
+      for (int i = 0; i < RSO_NCAND; ++i) cand_add(cand, fb_cand[i], &over);
+    }
+    over |= over2;
+  }
+  for (int i = 0; i < n_alt; ++i) cand_add(cand, alt[i], &over);
+  if (tie || fallback_fragile || winner_fragile) *flags |= RSO_FLAG_RACE_TIE;
+  if (over) *flags |= RSO_FLAG_CAND_OVERFLOW;
+  return token;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -323,7 +416,7 @@ int rso_verify_filtered(const void* logits, int32_t dtype, const float* q, const
                         const int32_t* cu, const float* T, const int32_t* top_k, const float* top_p,
                         int32_t B, int32_t D, int32_t max_k, int32_t V, uint64_t seed, int32_t greedy_only,
                         double eps, int32_t* out, int32_t* num_accepted, int32_t* flags, double* p_draft,
-                        int32_t nthreads) {
+                        int32_t* cand, int32_t nthreads) {
   if (!logits || !draft || !cu || !out || !num_accepted || !flags) return -1;
   if (!greedy_only && !T) return -1;
   if (B < 0 || D < 0 || V < 1 || max_k < 0 || (dtype != RSO_F32 && dtype != RSO_BF16)) return -1;
@@ -355,6 +448,9 @@ int rso_verify_filtered(const void* logits, int32_t dtype, const float* q, const
       for (int32_t i = 0; i <= max_k; ++i) ob[i] = -1;
       num_accepted[b] = -1;
       flags[b] = 0;
+      int32_t* cb = cand ? cand + (int64_t)b * RSO_NCAND : NULL;
+      if (cb)
+        for (int i = 0; i < RSO_NCAND; ++i) cb[i] = -1;
       int32_t s = cu[b], e = cu[b + 1];
       int32_t K = e - s;
       int valid = (s >= 0 && e <= D && K >= 0 && K <= max_k);
@@ -423,19 +519,7 @@ int rso_verify_filtered(const void* logits, int32_t dtype, const float* q, const
             rhi[x] = p[x] * (1.0 + eps);
           }
         }
-        int tie = 0;
-        token = race(r, rlo, rhi, V, seed, b, n, eps, E, &tie);
-        if (token < 0) {
-          /* all-zero residual: race over p at the same position */
-          flags[b] |= RSO_FLAG_ZERO_RESIDUAL;
-          for (int32_t x = 0; x < V; ++x) {
-            r[x] = p[x];
-            rlo[x] = p[x] * (1.0 - eps);
-            rhi[x] = p[x] * (1.0 + eps);
-          }
-          token = race(r, rlo, rhi, V, seed, b, n, eps, E, &tie);
-        }
-        if (tie) flags[b] |= RSO_FLAG_RACE_TIE;
+        token = sample_with_fallback(r, rlo, rhi, p, V, seed, b, n, eps, E, &flags[b], cb);
       }
       for (int32_t i = 0; i < n; ++i) ob[i] = draft[s + i];
       ob[n] = token;
@@ -450,9 +534,9 @@ int rso_verify_filtered(const void* logits, int32_t dtype, const float* q, const
 int rso_verify(const void* logits, int32_t dtype, const float* q, const int32_t* draft,
                const int32_t* cu, const float* T, int32_t B, int32_t D, int32_t max_k, int32_t V,
                uint64_t seed, int32_t greedy_only, double eps, int32_t* out, int32_t* num_accepted,
-               int32_t* flags, double* p_draft, int32_t nthreads) {
+               int32_t* flags, double* p_draft, int32_t* cand, int32_t nthreads) {
   return rso_verify_filtered(logits, dtype, q, draft, cu, T, NULL, NULL, B, D, max_k, V, seed, greedy_only,
-                             eps, out, num_accepted, flags, p_draft, nthreads);
+                             eps, out, num_accepted, flags, p_draft, cand, nthreads);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -490,7 +574,7 @@ int rso_verify(const void* logits, int32_t dtype, const float* q, const int32_t*
 int rso_verify_tree(const void* logits, int32_t dtype, const int32_t* tokens, const int32_t* parents,
                     const int32_t* cu, const float* T, int32_t B, int32_t N, int32_t max_nodes, int32_t max_depth,
                     int32_t V, uint64_t seed, double eps, int32_t* out, int32_t* path, int32_t* num_accepted,
-                    int32_t* flags, int32_t nthreads) {
+                    int32_t* flags, int32_t* cand, int32_t nthreads) {
   if (!logits || !cu || !T || !out || !path || !num_accepted || !flags) return -1;
   if (B < 0 || N < 0 || V < 1 || max_nodes < 0 || max_depth < 0 || (N > 0 && (!tokens || !parents))) return -1;
 #ifdef _OPENMP
@@ -521,6 +605,9 @@ int rso_verify_tree(const void* logits, int32_t dtype, const int32_t* tokens, co
       for (int32_t i = 0; i < max_depth; ++i) pb[i] = -1;
       num_accepted[b] = -1;
       flags[b] = 0;
+      int32_t* cb = cand ? cand + (int64_t)b * RSO_NCAND : NULL;
+      if (cb)
+        for (int i = 0; i < RSO_NCAND; ++i) cb[i] = -1;
       int32_t s = cu[b], e = cu[b + 1], n = e - s;
       int valid = (s >= 0 && e <= N && n >= 0 && n <= max_nodes);
       for (int32_t i = 0; valid && i < n; ++i) {
@@ -569,18 +656,7 @@ int rso_verify_tree(const void* logits, int32_t dtype, const int32_t* tokens, co
               rlo[x] = r[x] * (1.0 - eps);
               rhi[x] = r[x] * (1.0 + eps);
             }
-            int tie = 0;
-            token = race(r, rlo, rhi, V, seed, b, d, eps, E, &tie);
-            if (token < 0) { /* every token drafted: race over p */
-              flags[b] |= RSO_FLAG_ZERO_RESIDUAL;
-              for (int32_t x = 0; x < V; ++x) {
-                r[x] = p[x];
-                rlo[x] = p[x] * (1.0 - eps);
-                rhi[x] = p[x] * (1.0 + eps);
-              }
-              token = race(r, rlo, rhi, V, seed, b, d, eps, E, &tie);
-            }
-            if (tie) flags[b] |= RSO_FLAG_RACE_TIE;
+            token = sample_with_fallback(r, rlo, rhi, p, V, seed, b, d, eps, E, &flags[b], cb);
           }
         }
         if (next < 0) break;

@@ -1,10 +1,11 @@
 """Shared helpers for the GPU parity tests: run the HIP path through the C ABI
 and the CPU oracle on the same tensors, then compare.
 
-Bar (see the design notes): token ids and accepted counts bit-exact on every
-request the oracle does not flag as a near tie (decision margin < 1e-6
-relative); flagged requests only need valid output.  p(x*) within 1e-5
-relative of the oracle's fp64 value.
+Bar: token ids and accepted counts bit-exact on every request the oracle does
+not flag as a near tie (decision margin < 1e-6 relative).  A flagged request
+must still be valid and agree with the oracle on every decision that is not
+the near tie (check_flagged / compare_tree).  p(x*) within 1e-5 relative of
+the oracle's fp64 value.
 """
 from __future__ import annotations
 
@@ -64,6 +65,45 @@ def run_oracle(w: W.Workload, *, greedy_entry: bool = False) -> oracle.OracleRes
                          w.seed, w.max_k, top_k=w.top_k, top_p=w.top_p)
 
 
+def _logit(w, row: int, x: int) -> float:
+    return float(w.logits[row, x].float().item())
+
+
+def check_flagged(tokens: np.ndarray, num_accepted: np.ndarray, o: oracle.OracleResult, w: W.Workload,
+                  b: int) -> None:
+    """Validity of a request the oracle flags as a near tie.  Several outputs
+    are correct there, but every invalid one must still fail:
+      - 0 <= n <= K_b, the first n tokens are the request's drafts, then one
+        token in [0, V) with a finite target logit at row n, then -1;
+      - unless an accept test or the top-p boundary is the near tie, n is the
+        oracle's n (the accept decisions themselves are not in doubt);
+      - then, if the race is the near tie, the token is the oracle's winner or
+        one of its near-tied alternatives; otherwise it is the oracle's token."""
+    cu = w.cu_num_draft_tokens
+    s, e = int(cu[b]), int(cu[b + 1])
+    K = e - s
+    n = int(num_accepted[b])
+    row = tokens[b]
+    where = f"flagged request b={b} (flags {int(o.flags[b])}): gpu n={n} tokens={row.tolist()} " \
+            f"oracle n={int(o.num_accepted[b])} tokens={o.tokens[b].tolist()}"
+    assert 0 <= n <= K, where
+    drafts = w.draft_token_ids[s:s + n].cpu().numpy()
+    assert (row[:n] == drafts).all(), where
+    assert (row[n + 1:] == -1).all(), where
+    tok = int(row[n])
+    assert 0 <= tok < w.V, where
+    assert _logit(w, s + b + n, tok) > float("-inf"), where
+    f = int(o.flags[b])
+    if f & (oracle.FLAG_ACCEPT_TIE | oracle.FLAG_TOPP_TIE):
+        return
+    assert n == int(o.num_accepted[b]), where
+    if f & oracle.FLAG_RACE_TIE:
+        if not f & oracle.FLAG_CAND_OVERFLOW:
+            assert tok in set(int(c) for c in o.cand[b] if c >= 0), where + f" candidates={o.cand[b].tolist()}"
+    else:
+        assert tok == int(o.tokens[b, n]), where
+
+
 def compare(g: GpuResult, o: oracle.OracleResult, w: W.Workload, *, max_flag_frac: Optional[float] = None) -> dict:
     """Assert the parity bar; return a small report."""
     flagged = o.near_tie
@@ -75,17 +115,60 @@ def compare(g: GpuResult, o: oracle.OracleResult, w: W.Workload, *, max_flag_fra
             f"{bad.size} unflagged request(s) differ, first b={b}: gpu n={g.num_accepted[b]} "
             f"tokens={g.tokens[b].tolist()} oracle n={o.num_accepted[b]} tokens={o.tokens[b].tolist()} "
             f"flags={int(o.flags[b])}")
-    # flagged requests: only validity
-    ks = np.asarray(w.num_draft)
-    for b in np.nonzero(flagged)[0]:
-        n = int(g.num_accepted[b])
-        assert 0 <= n <= ks[b]
-        row = g.tokens[b]
-        assert 0 <= row[n] < w.V and (row[n + 1:] == -1).all()
+    fl = np.nonzero(flagged)[0]
+    if fl.size:
+        wc = w.to("cpu") if fl.size > 64 else w
+        for b in fl:
+            check_flagged(g.tokens, g.num_accepted, o, wc, int(b))
     frac = float(flagged.mean()) if flagged.size else 0.0
     if max_flag_frac is not None:
         assert frac <= max_flag_frac, f"flagged fraction {frac} > {max_flag_frac}"
     return {"requests": int(flagged.size), "flagged": int(flagged.sum()), "flag_frac": frac}
+
+
+def compare_tree(out: np.ndarray, path: np.ndarray, n: np.ndarray, o, tw, max_depth: int) -> int:
+    """Tree verify against the oracle: bit-exact on unflagged requests; on a
+    flagged one, a valid walk (each accepted node a child of the previous one,
+    its token emitted, then one token in [0, V), then -1), the oracle's depth
+    and path unless an accept coin is the near tie, and then the oracle's
+    token or, for a race near tie, one of its near-tied alternatives.
+    Returns the number of flagged requests."""
+    ok = ~o.near_tie
+    bad = np.nonzero(ok & ((n != o.num_accepted) | (out != o.tokens).any(1) | (path != o.path).any(1)))[0]
+    if bad.size:
+        b = int(bad[0])
+        raise AssertionError(f"{bad.size} unflagged requests differ; b={b}: gpu n={n[b]} out={out[b].tolist()} "
+                             f"path={path[b].tolist()} oracle n={o.num_accepted[b]} out={o.tokens[b].tolist()} "
+                             f"path={o.path[b].tolist()} flags={o.flags[b]}")
+    cu = tw.cu_num_nodes.cpu().numpy()
+    toks = tw.node_tokens.cpu().numpy()
+    pars = tw.node_parents.cpu().numpy()
+    for b in np.nonzero(~ok)[0]:
+        b = int(b)
+        s, e = int(cu[b]), int(cu[b + 1])
+        d = int(n[b])
+        where = f"flagged tree request b={b} (flags {int(o.flags[b])}): gpu d={d} out={out[b].tolist()} " \
+                f"path={path[b].tolist()} oracle d={int(o.num_accepted[b])} out={o.tokens[b].tolist()}"
+        assert 0 <= d <= max_depth, where
+        prev = -1
+        for i in range(d):
+            node = int(path[b, i])
+            assert 0 <= node < e - s and int(pars[s + node]) == prev, where
+            assert int(out[b, i]) == int(toks[s + node]), where
+            prev = node
+        assert (path[b, d:] == -1).all() and (out[b, d + 1:] == -1).all(), where
+        tok = int(out[b, d])
+        assert 0 <= tok < tw.V, where
+        f = int(o.flags[b])
+        if f & oracle.FLAG_ACCEPT_TIE:
+            continue
+        assert d == int(o.num_accepted[b]) and (path[b] == o.path[b]).all(), where
+        if f & oracle.FLAG_RACE_TIE:
+            if not f & oracle.FLAG_CAND_OVERFLOW:
+                assert tok in set(int(c) for c in o.cand[b] if c >= 0), where + f" candidates={o.cand[b].tolist()}"
+        else:
+            assert tok == int(o.tokens[b, d]), where
+    return int((~ok).sum())
 
 
 def compare_p(g: GpuResult, o: oracle.OracleResult, w: Optional[W.Workload] = None) -> float:

@@ -273,3 +273,121 @@ def test_race_near_tie_flag():
                           np.array([1.0], np.float32), seed, 0)
         assert bool(r.flags[0] & oracle.FLAG_RACE_TIE) == flagged
         assert r.tokens[0, 0] in (0, 1)
+
+
+# ------------------------------------------------------- all-zero residual
+def _zero_residual_batch(V, B, seed, q_of_p, T=1.0):
+    """K = 1 per request, all requests sharing one draft row and one bonus row;
+    q = q_of_p(p0) (fp32, not normalised), drafts drawn from p0."""
+    rng = np.random.default_rng(seed)
+    l0 = (rng.standard_normal(V) * 1.5).astype(np.float32)
+    l1 = (rng.standard_normal(V) * 1.5).astype(np.float32)
+    p0, p1 = _softmax(l0, T), _softmax(l1, T)
+    qv = np.asarray(q_of_p(p0), np.float32)
+    drafts = rng.choice(V, size=(B, 1), p=p0)
+    lg, q, d, cu, Tb = _batch(np.broadcast_to(np.stack([l0, l1]), (B, 2, V)), np.broadcast_to(qv, (B, 1, V)),
+                              drafts, np.full(B, T))
+    return oracle.verify(lg, q, d, cu, Tb, seed=seed, max_k=1), p0, p1, qv, drafts.reshape(-1)
+
+
+@pytest.mark.slow
+def test_zero_residual_q_twice_p_falls_back_to_p():
+    """q = 2p is not normalised; the library takes q as given (q >= 0 only).
+    The accept test u * 2p(x*) < p(x*) holds iff u < 1/2, so exactly half of
+    the drafts are accepted, whatever x*.  At a rejection max(0, p - q) is zero
+    everywhere and the residual of [Ch.12 §12.2.1 step 3] is undefined; the
+    reading races over p at the same position.  So: every rejected request,
+    and no other, carries FLAG_ZERO_RESIDUAL; the fallback is exact (no near
+    tie); the rejected trials' token follows p; the bonus follows the next
+    row's p; the first emitted token follows p overall."""
+    V, B = 8, N_TRIALS
+    r, p0, p1, qv, drafts = _zero_residual_batch(V, B, 23, lambda p: 2.0 * p)
+    rej = r.num_accepted == 0
+    assert abs(rej.mean() - 0.5) < 5 * 0.5 / np.sqrt(B)
+    zr = (r.flags & oracle.FLAG_ZERO_RESIDUAL) != 0
+    np.testing.assert_array_equal(zr, rej)
+    # near ties only from accept coins next to u = 1/2
+    # (|1 - 2u| <= 1e-6: a few grid points of 2^-24), or from genuine near ties
+    # of the fallback race's top two keys p / E
+    assert r.near_tie.sum() <= 10
+    for b in np.nonzero(r.near_tie)[0]:
+        if r.flags[b] & oracle.FLAG_RACE_TIE:
+            keys = np.sort(p0 / oracle.race_exponentials(23, int(b), 0, 0, V))
+            assert keys[-1] - keys[-2] <= 3e-6 * keys[-1]
+    assert _chi2_ok(np.bincount(r.tokens[rej, 0], minlength=V), p0) > PVAL
+    assert _chi2_ok(np.bincount(r.tokens[~rej, 1], minlength=V), p1) > PVAL
+    assert _chi2_ok(np.bincount(r.tokens[:, 0], minlength=V), p0) > PVAL
+    # the fallback's token is the race over p with the position's exponentials:
+    # recompute one rejected request's winner from the race definition
+    b = int(np.nonzero(rej)[0][0])
+    E = oracle.race_exponentials(23, b, 0, 0, V)
+    assert r.tokens[b, 0] == int(np.argmax(p0 / E))
+    assert r.cand[b, 0] == r.tokens[b, 0] and (r.cand[b, 1:] == -1).all()
+
+
+def test_zero_residual_fragile_is_a_race_near_tie():
+    """q(x*) = 2p(x*) (rejections), every other q(x) = p(x)(1 + 3e-7): the
+    residual is zero everywhere, but p(1 + 1e-6) - q > 0 for the other tokens,
+    so a perturbed p would race over them instead of falling back: the
+    request is a race near tie, and its candidates hold the fallback winner
+    and every token whose residual could be positive."""
+    V, B = 8, 4000
+
+    def q_of_p(p):
+        q = (p * (1 + 3e-7)).astype(np.float32)
+        assert (q.astype(np.float64) > p).all() and (q.astype(np.float64) < p * (1 + 1e-6)).all()
+        return q
+
+    rng = np.random.default_rng(5)
+    l0 = (rng.standard_normal(V) * 1.5).astype(np.float32)
+    l1 = (rng.standard_normal(V) * 1.5).astype(np.float32)
+    p0 = _softmax(l0)
+    xs = int(np.argmax(p0))
+    qv = q_of_p(p0)
+    qv[xs] = np.float32(2 * p0[xs])
+    drafts = np.full((B, 1), xs)
+    lg, q, d, cu, Tb = _batch(np.broadcast_to(np.stack([l0, l1]), (B, 2, V)), np.broadcast_to(qv, (B, 1, V)),
+                              drafts, np.full(B, 1.0))
+    r = oracle.verify(lg, q, d, cu, Tb, seed=7, max_k=1)
+    rej = r.num_accepted == 0
+    assert 0.4 < rej.mean() < 0.6
+    fl = r.flags[rej]
+    assert ((fl & oracle.FLAG_ZERO_RESIDUAL) != 0).all() and ((fl & oracle.FLAG_RACE_TIE) != 0).all()
+    others = [x for x in range(V) if x != xs]
+    for b in np.nonzero(rej)[0][:50]:
+        c = set(int(x) for x in r.cand[b] if x >= 0)
+        assert int(r.tokens[b, 0]) in c and set(others) <= c
+    assert (r.flags[~rej] & oracle.FLAG_ZERO_RESIDUAL == 0).all()
+
+
+def test_zero_residual_fragile_winner_is_a_race_near_tie():
+    """One token keeps a residual of 3e-7 p (q just below p) and wins the race
+    alone; under the perturbation that residual vanishes and the fallback
+    would race over p, so the request is a race near tie whose candidates hold
+    both winners; a residual of 1e-3 p is not."""
+    V, B = 8, 2000
+    rng = np.random.default_rng(9)
+    l0 = (rng.standard_normal(V) * 1.5).astype(np.float32)
+    l1 = (rng.standard_normal(V) * 1.5).astype(np.float32)
+    p0 = _softmax(l0)
+    order = np.argsort(p0)
+    xs, keep = int(order[-1]), int(order[0])
+    for rel, fragile in ((3e-7, True), (1e-3, False)):
+        qv = (2 * p0).astype(np.float32)
+        qv[keep] = np.float32(p0[keep] * (1 - rel))
+        assert qv[keep] < p0[keep]
+        drafts = np.full((B, 1), xs)
+        lg, q, d, cu, Tb = _batch(np.broadcast_to(np.stack([l0, l1]), (B, 2, V)), np.broadcast_to(qv, (B, 1, V)),
+                                  drafts, np.full(B, 1.0))
+        r = oracle.verify(lg, q, d, cu, Tb, seed=11, max_k=1)
+        rej = r.num_accepted == 0
+        assert rej.any()
+        assert (r.tokens[rej, 0] == keep).all()  # the only positive residual
+        assert not (r.flags[rej] & oracle.FLAG_ZERO_RESIDUAL).any()
+        tie = (r.flags[rej] & oracle.FLAG_RACE_TIE) != 0
+        assert tie.all() if fragile else not tie.any()
+        if fragile:
+            for b in np.nonzero(rej)[0][:50]:
+                E = oracle.race_exponentials(11, int(b), 0, 0, V)
+                fb = int(np.argmax(p0 / E))
+                assert keep in r.cand[b] and fb in r.cand[b]

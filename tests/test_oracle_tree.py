@@ -143,3 +143,24 @@ def test_invalid_trees():
     assert (r.num_accepted == -1).all() and (r.tokens == -1).all()
     r = oracle.verify_tree(lg, tokens, parents, cu, np.ones(4, np.float32), 0, 3, 3)
     assert (r.flags & oracle.FLAG_INVALID).tolist() == [0, 8, 8, 0]
+
+
+def test_every_token_drafted_never_reaches_the_zero_residual():
+    """In a tree the post-rejection residual is p without the stop node's
+    children.  It is all zero only if the children cover every token of
+    positive p, but then their accumulated p is 1 (up to fp64 rounding) and the
+    coin u < 1 always accepts one of them [端到端深挖 §7.2]: a rejection means
+    the uncovered tokens carry at least 1 - u >= 2^-24 of the mass.  So the
+    tree's zero-residual fallback is unreachable; with every one of V tokens
+    drafted at every node no request stops there or takes the fallback."""
+    V, B = 8, 3000
+    rng = np.random.default_rng(4)
+    parents = [-1] * V + list(range(V))          # every token at the root, then one child each
+    tokens = list(range(V)) + list(rng.integers(0, V, size=V))
+    n = len(parents)
+    lg = (rng.standard_normal((B * (n + 1), V)) * 2).astype(np.float32)
+    cu = np.arange(B + 1, dtype=np.int32) * n
+    r = oracle.verify_tree(lg, np.tile(np.array(tokens, np.int32), B), np.tile(np.array(parents, np.int32), B), cu,
+                           np.full(B, 0.9, np.float32), 3, n, 3)
+    assert (r.num_accepted >= 1).all()
+    assert not (r.flags & oracle.FLAG_ZERO_RESIDUAL).any()

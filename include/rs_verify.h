@@ -170,6 +170,31 @@ rs_status rs_verify(const void* target_logits, rs_dtype logits_dtype, const floa
                     int32_t* num_accepted, void* workspace, size_t workspace_bytes,
                     const rs_debug* debug, hipStream_t stream);
 
+/* rs_verify for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * takes no workspace; its scratch is an array of RS_NOALLOC_SCRATCH_BYTES in
+ * the library's own device code object, one per GPU the library runs on, held
+ * until the process ends.  The call allocates nothing (no hipMalloc, hipFree
+ * or allocating library routine).  Arguments, layout, outputs, ownership and
+ * errors are those of rs_verify; in addition:
+ *   - a call whose rs_verify_workspace_size(...) exceeds
+ *     RS_NOALLOC_SCRATCH_BYTES returns RS_ERR_WORKSPACE before any HIP call
+ *     (8 MiB holds every measured workload, e.g. B=512, K=8, V=151936 with
+ *     bf16 logits or B=256 with fp32 logits; not B=1024 or B=512 fp32);
+ *   - the first call on a device, with that device current, looks the
+ *     array's device address up (hipGetSymbolAddress); `stream` must belong to
+ *     the current device;
+ *   - every call on one GPU shares that GPU's array: calls that overlap on one
+ *     GPU (concurrent streams, or threads) race and give wrong results; calls
+ *     ordered on one stream are safe, each call leaving the array in whatever
+ *     state and the next one initialising what it needs. */
+#define RS_NOALLOC_SCRATCH_BYTES (8u << 20)
+rs_status rs_verify_noalloc(const void* target_logits, rs_dtype logits_dtype, const float* draft_probs,
+                            const int32_t* draft_token_ids, const int32_t* cu_num_draft_tokens,
+                            const float* temperature, int32_t batch, int32_t total_draft_tokens, int32_t max_k,
+                            int32_t vocab, uint64_t seed, int32_t* output_token_ids, int32_t* num_accepted,
+                            const rs_debug* debug, hipStream_t stream);
+
 /* rs_verify with top-k / top-p filtering of each random request's target
  * distribution before the accept test, the residual and the bonus: the
  * rejection sampler constrains the target distribution with temperature,

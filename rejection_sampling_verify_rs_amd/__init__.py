@@ -18,8 +18,8 @@ from typing import Optional, Sequence, Tuple
 
 import torch
 
-__all__ = ["verify", "verify_greedy", "workspace_size", "Debug", "RsVerifyError", "load_library",
-           "accept_stats_accumulate", "accept_rate", "accept_length", "verify_tree", "MAX_SPEC_LEN",
+__all__ = ["verify", "verify_greedy", "verify_noalloc", "workspace_size", "NOALLOC_SCRATCH_BYTES", "Debug",
+           "RsVerifyError", "load_library", "accept_stats_accumulate", "accept_rate", "accept_length", "verify_tree", "MAX_SPEC_LEN",
            "MAX_TREE_NODES", "STATS_COUNTERS", "ngram_propose",
            "LIB_PATH"]
 
@@ -28,6 +28,7 @@ MAX_SPEC_LEN = 32
 MAX_TREE_NODES = 64
 STATS_SCALARS = 5
 STATS_COUNTERS = STATS_SCALARS + MAX_SPEC_LEN
+NOALLOC_SCRATCH_BYTES = 8 << 20  # RS_NOALLOC_SCRATCH_BYTES
 
 RS_OK, RS_ERR_INVALID_ARG, RS_ERR_UNSUPPORTED, RS_ERR_WORKSPACE, RS_ERR_HIP = range(5)
 RS_F32, RS_BF16 = 0, 1
@@ -72,6 +73,8 @@ def load_library(path: str = LIB_PATH):
     lib.rs_verify_filtered_workspace_size.restype = sz
     lib.rs_verify.argtypes = [P, ctypes.c_int, P, P, P, P, i32, i32, i32, i32, u64, P, P, P, sz, P, P]
     lib.rs_verify.restype = ctypes.c_int
+    lib.rs_verify_noalloc.argtypes = [P, ctypes.c_int, P, P, P, P, i32, i32, i32, i32, u64, P, P, P, P]
+    lib.rs_verify_noalloc.restype = ctypes.c_int
     lib.rs_verify_filtered.argtypes = [P, ctypes.c_int, P, P, P, P, P, P, i32, i32, i32, i32, u64, P, P, P, sz, P,
                                        P]
     lib.rs_verify_filtered.restype = ctypes.c_int
@@ -244,6 +247,57 @@ def verify(target_logits: torch.Tensor, draft_probs: Optional[torch.Tensor], dra
     else:
         status = lib.rs_verify_filtered(*head, top_k.data_ptr() if top_k is not None else None,
                                         top_p.data_ptr() if top_p is not None else None, *tail)
+    if debug is not None:
+        debug.kernels_launched = int(keep[0].value)
+        debug.path_taken = int(keep[1].value)
+    del keep
+    _check(status)
+    return out, num_accepted
+
+
+def verify_noalloc(target_logits: torch.Tensor, draft_probs: Optional[torch.Tensor], draft_token_ids: torch.Tensor,
+                   cu_num_draft_tokens: torch.Tensor, temperature: torch.Tensor, *, seed: int, max_k: int,
+                   out: torch.Tensor, num_accepted: torch.Tensor, debug: Optional[Debug] = None,
+                   stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """rs_verify_noalloc: rs_verify with the library's own fixed scratch and no
+    workspace argument, for callers that cannot allocate.  The caller passes
+    the outputs (out [B, max_k+1] int32, num_accepted [B] int32); this binding
+    allocates nothing either.  Calls that overlap on one GPU race on the
+    shared scratch."""
+    lib = load_library()
+    if not isinstance(target_logits, torch.Tensor) or target_logits.device.type != "cuda":
+        raise ValueError("target_logits must be a CUDA (HIP) tensor")
+    if target_logits.dtype not in _DTYPE:
+        raise TypeError(f"target_logits must be float32 or bfloat16, got {target_logits.dtype}")
+    dev = target_logits.device
+    _dev_tensor(target_logits, "target_logits", None, dev)
+    _dev_tensor(draft_token_ids, "draft_token_ids", torch.int32, dev)
+    _dev_tensor(cu_num_draft_tokens, "cu_num_draft_tokens", torch.int32, dev)
+    _dev_tensor(temperature, "temperature", torch.float32, dev)
+    _dev_tensor(out, "out", torch.int32, dev)
+    _dev_tensor(num_accepted, "num_accepted", torch.int32, dev)
+    V = int(target_logits.shape[-1])
+    B = int(cu_num_draft_tokens.numel()) - 1
+    D = int(draft_token_ids.numel())
+    if B < 0 or target_logits.numel() != (D + B) * V or temperature.numel() != B:
+        raise ValueError("expected target_logits [D + B, V], temperature [B], cu_num_draft_tokens [B + 1]")
+    if out.numel() != B * (max_k + 1) or num_accepted.numel() != B:
+        raise ValueError("out must hold B * (max_k + 1) and num_accepted B int32 values")
+    if draft_probs is not None:
+        _dev_tensor(draft_probs, "draft_probs", torch.float32, dev)
+        if draft_probs.numel() != D * V:
+            raise ValueError("draft_probs must be [D, V]")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    dbg, keep = (None, None)
+    if debug is not None:
+        dbg, keep = debug._struct(stream)
+    status = lib.rs_verify_noalloc(
+        target_logits.data_ptr(), _DTYPE[target_logits.dtype],
+        draft_probs.data_ptr() if draft_probs is not None else None, draft_token_ids.data_ptr() if D > 0 else None,
+        cu_num_draft_tokens.data_ptr(), temperature.data_ptr(), B, D, int(max_k), V, int(seed) & ((1 << 64) - 1),
+        out.data_ptr(), num_accepted.data_ptr(), ctypes.byref(dbg) if dbg is not None else None,
+        ctypes.c_void_p(stream.cuda_stream))
     if debug is not None:
         debug.kernels_launched = int(keep[0].value)
         debug.path_taken = int(keep[1].value)

@@ -42,6 +42,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "common.hpp"
 #include "filter.hpp"
 #include "philox.hpp"
@@ -587,10 +589,35 @@ static rs_status launch(const void* logits_v, const float* q, const int32_t* dra
   return RS_OK;
 }
 
+// ---------------------------------------------------- library-owned scratch
+// rs_verify_noalloc's workspace: one array per GPU, in the library's code
+// object, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory; its device address is looked up once
+// per device (hipGetSymbolAddress, with that device current) and only that
+// address is ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[RS_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+// Device address of the current device's scratch array.
+static rs_status library_scratch(void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return RS_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return RS_ERR_UNSUPPORTED;
+  void* a = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!a) {
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return RS_ERR_HIP;
+    g_scratch_addr[dev].store(a, std::memory_order_release);  // racing first calls store the same address
+  }
+  *addr = a;
+  return RS_OK;
+}
+
 static rs_status verify_impl(const void* logits, rs_dtype dt, const float* q, const int32_t* draft, const int32_t* cu,
                              const float* temperature, const int32_t* top_k, const float* top_p, int greedy_all,
                              int32_t B, int32_t D, int32_t max_k, int32_t V, uint64_t seed, int32_t* out,
-                             int32_t* nacc, void* ws, size_t ws_bytes, const rs_debug* dbg, hipStream_t stream) {
+                             int32_t* nacc, void* ws, size_t ws_bytes, const rs_debug* dbg, hipStream_t stream,
+                             bool lib_scratch = false) {
   // Every check below runs before the first HIP call.
   if (B < 0 || D < 0 || V < 1 || max_k < 0) return RS_ERR_INVALID_ARG;
   if (dt != RS_F32 && dt != RS_BF16) return RS_ERR_UNSUPPORTED;
@@ -616,6 +643,12 @@ static rs_status verify_impl(const void* logits, rs_dtype dt, const float* q, co
   }
   Plan p;
   if (!make_plan(B, D, max_k, V, dt, dbg, !greedy_all && (top_k || top_p), p)) return RS_ERR_UNSUPPORTED;
+  if (lib_scratch) {  // the library's own array instead of a caller's workspace
+    if (p.total > RS_NOALLOC_SCRATCH_BYTES) return RS_ERR_WORKSPACE;
+    const rs_status st = library_scratch(&ws);
+    if (st != RS_OK) return st;
+    ws_bytes = RS_NOALLOC_SCRATCH_BYTES;
+  }
   if (!ws || !aligned(ws, 16) || ws_bytes < p.total) return RS_ERR_WORKSPACE;
   if (dt == RS_BF16)
     return launch<uint16_t>(logits, q, draft, cu, temperature, top_k, top_p, greedy_all, B, D, max_k, V, seed, out,
@@ -656,6 +689,16 @@ rs_status rs_verify(const void* target_logits, rs_dtype logits_dtype, const floa
   return rsv::verify_impl(target_logits, logits_dtype, draft_probs, draft_token_ids, cu_num_draft_tokens, temperature,
                           nullptr, nullptr, 0, batch, total_draft_tokens, max_k, vocab, seed, output_token_ids,
                           num_accepted, workspace, workspace_bytes, debug, stream);
+}
+
+rs_status rs_verify_noalloc(const void* target_logits, rs_dtype logits_dtype, const float* draft_probs,
+                            const int32_t* draft_token_ids, const int32_t* cu_num_draft_tokens,
+                            const float* temperature, int32_t batch, int32_t total_draft_tokens, int32_t max_k,
+                            int32_t vocab, uint64_t seed, int32_t* output_token_ids, int32_t* num_accepted,
+                            const rs_debug* debug, hipStream_t stream) {
+  return rsv::verify_impl(target_logits, logits_dtype, draft_probs, draft_token_ids, cu_num_draft_tokens, temperature,
+                          nullptr, nullptr, 0, batch, total_draft_tokens, max_k, vocab, seed, output_token_ids,
+                          num_accepted, nullptr, 0, debug, stream, true);
 }
 
 rs_status rs_verify_filtered(const void* target_logits, rs_dtype logits_dtype, const float* draft_probs,
@@ -803,7 +846,8 @@ const char* rs_status_string(rs_status status) {
     case RS_ERR_UNSUPPORTED:
       return "RS_ERR_UNSUPPORTED: unsupported dtype, alignment or size";
     case RS_ERR_WORKSPACE:
-      return "RS_ERR_WORKSPACE: workspace missing, misaligned or too small";
+      return "RS_ERR_WORKSPACE: workspace missing, misaligned or too small (rs_verify_noalloc: the call needs more "
+             "than the library's RS_NOALLOC_SCRATCH_BYTES of scratch)";
     case RS_ERR_HIP:
       return "RS_ERR_HIP: a HIP launch or event call failed";
   }

@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
                                      "rs_accept_stats_accumulate", "rs_ngram_propose", "rs_status_string",
                                      "rs_verify",
                                      "rs_verify_filtered", "rs_verify_filtered_workspace_size", "rs_verify_greedy",
-                                     "rs_verify_tree", "rs_verify_tree_workspace_size", "rs_verify_workspace_size"]
+                                     "rs_verify_noalloc", "rs_verify_tree", "rs_verify_tree_workspace_size",
+                                     "rs_verify_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -138,6 +139,30 @@ def test_debug_knobs_validated(lib):
     d.sampling_path = 0
     d.num_events = 3  # events array missing
     assert _call(lib, dbg=ctypes.byref(d)) == rs.RS_ERR_INVALID_ARG
+
+
+@needs_no_gpu
+def test_noalloc_entry_validation(lib):
+    """rs_verify_noalloc: the argument checks of rs_verify, and a call whose
+    workspace would exceed the library's fixed scratch is refused, all before
+    any HIP call."""
+    f = lib.rs_verify_noalloc
+    ok = dict(logits=DUMMY, dtype=1, q=None, draft=DUMMY, cu=DUMMY, T=DUMMY, B=2, D=4, max_k=2, V=100, seed=0,
+              out=DUMMY, nacc=DUMMY)
+
+    def g(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["logits"], a["dtype"], a["q"], a["draft"], a["cu"], a["T"], a["B"], a["D"], a["max_k"], a["V"],
+                 a["seed"], a["out"], a["nacc"], None, None)
+
+    assert g(max_k=40) == rs.RS_ERR_INVALID_ARG
+    assert g(cu=None) == rs.RS_ERR_INVALID_ARG
+    assert g(dtype=7) == rs.RS_ERR_UNSUPPORTED
+    assert g(B=0, D=0) == rs.RS_OK
+    B, K, V = 1024, 8, 151936
+    assert rs.workspace_size(B, B * K, K, V) > rs.NOALLOC_SCRATCH_BYTES >= rs.workspace_size(512, 512 * K, K, V)
+    assert g(B=B, D=B * K, max_k=K, V=V) == rs.RS_ERR_WORKSPACE
 
 
 @needs_no_gpu

@@ -44,6 +44,19 @@ def test_library_exports_every_declared_symbol(lib):
     assert lib.rs_abi_version() == 1
 
 
+def test_status_codes_as_documented(lib):
+    """The status codes the header declares (RS_ERR_WORKSPACE = 3 and
+    RS_ERR_HIP = 4, a departure from the survey's sketch recorded in the
+    design notes), their strings and the binding's constants."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    enum = dict((k, int(v)) for k, v in re.findall(r"\b(RS_(?:OK|ERR_[A-Z_]+))\s*=\s*(\d+)", src))
+    assert enum == {"RS_OK": 0, "RS_ERR_INVALID_ARG": 1, "RS_ERR_UNSUPPORTED": 2, "RS_ERR_WORKSPACE": 3,
+                    "RS_ERR_HIP": 4}
+    for name, code in enum.items():
+        assert lib.rs_status_string(code).decode().split(":")[0] == name
+        assert getattr(rs, name) == code
+
+
 def test_status_strings(lib):
     for code in range(5):
         assert lib.rs_status_string(code).decode().startswith("RS_")

@@ -79,15 +79,19 @@ extern "C" {
 #define RS_VERIFY_ABI_VERSION 1
 #define RS_MAX_SPEC_LEN 32 /* [第12章 §12.5.4: MAX_SPEC_LEN = 32] */
 
+/* Both enums span every 32-bit value (the *_ENUM_MAX sentinels), so any int a
+ * caller passes is a valid value of the type; unknown values are reported,
+ * not undefined. */
 typedef enum rs_status {
   RS_OK = 0,
   RS_ERR_INVALID_ARG = 1, /* NULL pointer, negative size, max_k > 32, D > B*max_k, ... */
   RS_ERR_UNSUPPORTED = 2, /* unknown dtype, misaligned pointer, size beyond the grid */
   RS_ERR_WORKSPACE = 3,   /* workspace NULL, misaligned or smaller than required */
-  RS_ERR_HIP = 4          /* a kernel launch or event record failed */
+  RS_ERR_HIP = 4,         /* a kernel launch or event record failed */
+  RS_STATUS_ENUM_MAX = 0x7FFFFFFF
 } rs_status;
 
-typedef enum rs_dtype { RS_F32 = 0, RS_BF16 = 1 } rs_dtype;
+typedef enum rs_dtype { RS_F32 = 0, RS_BF16 = 1, RS_DTYPE_ENUM_MAX = 0x7FFFFFFF } rs_dtype;
 
 /* Optional outputs and knobs for parity checks and profiling.  Pass NULL in
  * production.  Every pointer may be NULL independently. */

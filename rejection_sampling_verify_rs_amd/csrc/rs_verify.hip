@@ -850,6 +850,8 @@ const char* rs_status_string(rs_status status) {
              "than the library's RS_NOALLOC_SCRATCH_BYTES of scratch)";
     case RS_ERR_HIP:
       return "RS_ERR_HIP: a HIP launch or event call failed";
+    default:
+      break;
   }
   return "unknown rs_status";
 }

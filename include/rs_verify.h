@@ -280,9 +280,9 @@ rs_status rs_verify_greedy(const void* target_logits, rs_dtype logits_dtype,
  * <= max_nodes the depth (a node with no parent has depth 0); a request whose
  * tree breaks these rules (too many nodes, a parent after its child, a token
  * out of range, a node of depth >= max_depth) gets -1 rows and
- * num_accepted = -1.  One workgroup per request walks the tree, streaming
- * only the rows on its accepted path and the stop row; the final race of
- * random requests is spread over the GPU.
+ * num_accepted = -1.  The walks run spread over the GPU: the rows of a
+ * walk's next candidates are streamed by many workgroups ahead of the step
+ * that needs them, and the stop row's race is split over the GPU too.
  *   workspace  >= rs_verify_tree_workspace_size(B, V) bytes, 16-byte aligned
  *              (RS_ERR_WORKSPACE otherwise); calls sharing one workspace must
  *              not overlap.

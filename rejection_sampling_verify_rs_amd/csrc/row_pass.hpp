@@ -237,8 +237,9 @@ __device__ __forceinline__ RowStats row_stats(const Elem* __restrict__ prow, int
 }
 
 // Statistics of chunk c (NV vectors per thread) of logits row `row`,
-// written to partials[row * nsplit + c].  Chunk 0 of a draft position's row
-// also stores l(x*) and q(x*) in *gath (x* = xstar, checked by the caller).
+// written to row_partials[c] (the row's nsplit partial slots).  Chunk 0 of a
+// draft position's row also stores l(x*) and q(x*) in *gath (x* = xstar,
+// checked by the caller).
 //
 // tmax (NULL: not wanted) receives every thread's own maximum of the chunk
 // (kRowThreads floats, -inf for a thread with no element): the top-k / top-p
@@ -246,7 +247,7 @@ __device__ __forceinline__ RowStats row_stats(const Elem* __restrict__ prow, int
 template <typename Elem, int NV, bool COH = false>
 __device__ __forceinline__ void chunk_task(const Elem* __restrict__ logits, const float* __restrict__ q, int64_t row,
                                            float T, int32_t V, int32_t nsplit, int32_t c, int32_t xstar,
-                                           int64_t slot, RowPartial* __restrict__ partials,
+                                           int64_t slot, RowPartial* __restrict__ row_partials,
                                            Gathered* __restrict__ gath, float* __restrict__ tmax = nullptr) {
   using VT = Vec<Elem>;
   constexpr int W = VT::W;
@@ -299,7 +300,7 @@ __device__ __forceinline__ void chunk_task(const Elem* __restrict__ logits, cons
   if (tmax) tmax[tid] = m;
   m = block_reduce<kRowThreads>(m, lds_f, MaxOp());
 
-  RowPartial* out = partials + row * nsplit + c;
+  RowPartial* out = row_partials + c;
   if (greedy) {
     int idx = INT_MAX;
     if (m > -INFINITY) {

@@ -42,6 +42,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "common.hpp"
@@ -126,7 +127,8 @@ __global__ __launch_bounds__(kRowThreads) void phase_kernel(
     const int64_t row = (int64_t)s + b + j;
     // a filtered row also leaves its segment maxima for the filter kernel
     float* tmax = (T > 0.f && filter_on(top_k, top_p, b, V)) ? tmaxbuf + (row * nsplit + c) * kRowThreads : nullptr;
-    chunk_task<Elem, NV>(logits, q, row, T, V, nsplit, c, xstar, (int64_t)s + j, partials, gath, tmax);
+    chunk_task<Elem, NV>(logits, q, row, T, V, nsplit, c, xstar, (int64_t)s + j, partials + row * nsplit, gath,
+                         tmax);
   } else {
     const int32_t c = t % race_chunks;
     const int32_t b = t / race_chunks;
@@ -657,6 +659,73 @@ static rs_status verify_impl(const void* logits, rs_dtype dt, const float* q, co
                        ws, p, dbg, stream);
 }
 
+// Tree workspace: walk words, per-step arrival counters and partial
+// statistics (for up to RS_MAX_TREE_NODES + 1 steps), race winners, records.
+struct TreeLayout {
+  int32_t nsplit_max, race_chunks;
+  size_t off_walk, off_count, off_claim, off_race_count, off_partials, off_cand, off_records, total;
+};
+
+static TreeLayout tree_layout(int32_t batch, int32_t vocab) {
+  TreeLayout t;
+  const int64_t vec_f32 = vocab / 4;  // fp32 rows have the most 16-byte vectors
+  t.nsplit_max = (int32_t)std::max<int64_t>(1, (vec_f32 + kTreeNV * kRowThreads - 1) /
+                                                   (kTreeNV * kRowThreads));
+  constexpr int32_t kChunk = kRaceThreads * kTreeRaceTPT;
+  t.race_chunks = (vocab + kChunk - 1) / kChunk;
+  const size_t B = (size_t)batch, L = kTreeMaxLayers;
+  t.off_walk = 0;
+  t.off_count = align_up(B * sizeof(unsigned long long));
+  t.off_claim = t.off_count + align_up(B * L * kTreeSlots * sizeof(uint32_t));
+  t.off_race_count = t.off_claim + align_up(B * L * sizeof(uint32_t));
+  t.off_partials = t.off_race_count + align_up(B * sizeof(uint32_t));
+  t.off_cand = t.off_partials + align_up(B * L * kTreeSlots * (size_t)t.nsplit_max * sizeof(RowPartial));
+  t.off_records = t.off_cand + align_up(B * (size_t)t.race_chunks * sizeof(unsigned long long));
+  t.total = t.off_records + align_up(B * sizeof(ReqRecord));
+  return t;
+}
+
+template <typename Elem>
+static rs_status launch_tree(const void* logits, const int32_t* node_tokens, const int32_t* node_parents,
+                             const int32_t* cu, const float* temperature, int32_t B, int32_t N, int32_t max_nodes,
+                             int32_t max_depth, int32_t V, uint64_t seed, int32_t* out, int32_t* path,
+                             int32_t* nacc, void* ws, hipStream_t stream) {
+  const TreeLayout t = tree_layout(B, V);
+  char* w = static_cast<char*>(ws);
+  TreeArgs<Elem> a;
+  a.logits = static_cast<const Elem*>(logits);
+  a.tokens = node_tokens;
+  a.parents = node_parents;
+  a.cu = cu;
+  a.temperature = temperature;
+  a.seed = seed;
+  a.B = B;
+  a.N = N;
+  a.max_nodes = max_nodes;
+  a.max_depth = max_depth;
+  a.V = V;
+  const int64_t nvec = V / Vec<Elem>::W;
+  a.nsplit = (int32_t)std::max<int64_t>(1, (nvec + kTreeNV * kRowThreads - 1) /
+                                               (kTreeNV * kRowThreads));
+  a.race_chunks = t.race_chunks;
+  a.out = out;
+  a.path = path;
+  a.nacc = nacc;
+  a.walk = reinterpret_cast<unsigned long long*>(w + t.off_walk);
+  a.count = reinterpret_cast<uint32_t*>(w + t.off_count);
+  a.claim = reinterpret_cast<uint32_t*>(w + t.off_claim);
+  a.race_count = reinterpret_cast<uint32_t*>(w + t.off_race_count);
+  a.partials = reinterpret_cast<RowPartial*>(w + t.off_partials);
+  a.cand = reinterpret_cast<unsigned long long*>(w + t.off_cand);
+  a.records = reinterpret_cast<ReqRecord*>(w + t.off_records);
+  tree_init_kernel<<<(unsigned)B, 64, 0, stream>>>(node_tokens, node_parents, cu, N, max_nodes, max_depth, V,
+                                                         out, path, nacc, a.walk, a.count, a.claim, a.race_count);
+  if (hipGetLastError() != hipSuccess) return RS_ERR_HIP;
+  const int64_t blocks = (int64_t)B * a.nsplit * (1 + (int64_t)kTreeSlots * max_depth) + (int64_t)B * a.race_chunks;
+  tree_walk_kernel<Elem, kTreeNV><<<(unsigned)blocks, kRowThreads, 0, stream>>>(a);
+  return hipGetLastError() == hipSuccess ? RS_OK : RS_ERR_HIP;
+}
+
 }  // namespace rsv
 
 extern "C" {
@@ -721,16 +790,10 @@ rs_status rs_verify_greedy(const void* target_logits, rs_dtype logits_dtype, con
                           num_accepted, workspace, workspace_bytes, nullptr, stream);
 }
 
-static int32_t tree_chunks(int32_t vocab) {
-  constexpr int32_t kChunk = rsv::kRaceThreads * rsv::kTreeRaceTPT;
-  return (vocab + kChunk - 1) / kChunk;
-}
-
 size_t rs_verify_tree_workspace_size(int32_t batch, int32_t vocab) {
   if (batch < 0 || vocab < 1) return 0;
   if (batch == 0) return 0;
-  const size_t rec = ((size_t)batch * sizeof(rsv::ReqRecord) + 255) / 256 * 256;
-  return rec + (size_t)batch * tree_chunks(vocab) * sizeof(unsigned long long);
+  return rsv::tree_layout(batch, vocab).total;
 }
 
 rs_status rs_verify_tree(const void* target_logits, rs_dtype logits_dtype, const int32_t* node_tokens,
@@ -752,42 +815,19 @@ rs_status rs_verify_tree(const void* target_logits, rs_dtype logits_dtype, const
       ((uintptr_t)cu_num_nodes % 4) || ((uintptr_t)temperature % 4) || ((uintptr_t)output_token_ids % 4) ||
       ((uintptr_t)accepted_nodes % 4) || ((uintptr_t)num_accepted % 4))
     return RS_ERR_UNSUPPORTED;
-  if (!workspace || ((uintptr_t)workspace % 16) || workspace_bytes < rs_verify_tree_workspace_size(batch, vocab))
-    return RS_ERR_WORKSPACE;
-  rsv::ReqRecord* records = static_cast<rsv::ReqRecord*>(workspace);
-  unsigned long long* cand = reinterpret_cast<unsigned long long*>(
-      static_cast<char*>(workspace) + ((size_t)batch * sizeof(rsv::ReqRecord) + 255) / 256 * 256);
-  const int32_t nchunks = tree_chunks(vocab);
-  const bool big = vocab >= 65536;
-#define RS_TREE(ELEM, NT)                                                                                          \
-  rsv::tree_kernel<ELEM, NT><<<(unsigned)batch, NT, 0, stream>>>(                                                 \
-      static_cast<const ELEM*>(target_logits), node_tokens, node_parents, cu_num_nodes, temperature, total_nodes, \
-      max_nodes, max_depth, vocab, seed, output_token_ids, accepted_nodes, num_accepted, records)
-#define RS_TREE_RACE(ELEM)                                                                                         \
-  rsv::tree_race_kernel<ELEM><<<(unsigned)((int64_t)batch * nchunks), rsv::kRaceThreads, 0, stream>>>(            \
-      static_cast<const ELEM*>(target_logits), node_tokens, node_parents, vocab, seed, nchunks, records, cand);    \
-  if (hipGetLastError() != hipSuccess) return RS_ERR_HIP;                                                          \
-  rsv::tree_emit_kernel<ELEM><<<(unsigned)batch, 64, 0, stream>>>(static_cast<const ELEM*>(target_logits),        \
-                                                                  max_depth, vocab, seed, nchunks, records, cand, \
-                                                                  output_token_ids, num_accepted)
-  if (logits_dtype == RS_BF16) {
-    if (big)
-      RS_TREE(uint16_t, 512);
-    else
-      RS_TREE(uint16_t, 256);
-    if (hipGetLastError() != hipSuccess) return RS_ERR_HIP;
-    RS_TREE_RACE(uint16_t);
-  } else {
-    if (big)
-      RS_TREE(float, 512);
-    else
-      RS_TREE(float, 256);
-    if (hipGetLastError() != hipSuccess) return RS_ERR_HIP;
-    RS_TREE_RACE(float);
-  }
-#undef RS_TREE
-#undef RS_TREE_RACE
-  return hipGetLastError() == hipSuccess ? RS_OK : RS_ERR_HIP;
+  // 1-D grid below 2^31 workgroups
+  const rsv::TreeLayout t = rsv::tree_layout(batch, vocab);
+  if ((int64_t)batch * t.nsplit_max * (1 + (int64_t)rsv::kTreeSlots * max_depth) + (int64_t)batch * t.race_chunks >=
+      INT32_MAX)
+    return RS_ERR_UNSUPPORTED;
+  if (!workspace || ((uintptr_t)workspace % 16) || workspace_bytes < t.total) return RS_ERR_WORKSPACE;
+  if (logits_dtype == RS_BF16)
+    return rsv::launch_tree<uint16_t>(target_logits, node_tokens, node_parents, cu_num_nodes, temperature, batch,
+                                 total_nodes, max_nodes, max_depth, vocab, seed, output_token_ids, accepted_nodes,
+                                 num_accepted, workspace, stream);
+  return rsv::launch_tree<float>(target_logits, node_tokens, node_parents, cu_num_nodes, temperature, batch, total_nodes,
+                            max_nodes, max_depth, vocab, seed, output_token_ids, accepted_nodes, num_accepted,
+                            workspace, stream);
 }
 
 rs_status rs_ngram_propose(const int32_t* context_token_ids, const int32_t* cu_context, int32_t batch,

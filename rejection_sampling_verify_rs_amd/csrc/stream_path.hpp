@@ -254,7 +254,8 @@ __device__ __forceinline__ void stream_row_task(const StreamArgs<Elem>& a, int32
   }
   const int32_t xstar = (c == 0 && j < K && T > 0.f) ? a.draft[s + j] : -1;
   const int64_t row = (int64_t)s + b + j;
-  chunk_task<Elem, NV, true>(a.logits, a.q, row, T, a.V, a.nsplit, c, xstar, (int64_t)s + j, a.partials, a.gath);
+  chunk_task<Elem, NV, true>(a.logits, a.q, row, T, a.V, a.nsplit, c, xstar, (int64_t)s + j,
+                             a.partials + row * a.nsplit, a.gath);
   if (tid >= 64) return;  // wavefront 0 reports the chunk
   int last = 0;
   if (tid == 0) {

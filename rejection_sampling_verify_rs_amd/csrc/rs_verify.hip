@@ -663,26 +663,48 @@ static rs_status verify_impl(const void* logits, rs_dtype dt, const float* q, co
 // statistics (for up to RS_MAX_TREE_NODES + 1 steps), race winners, records.
 struct TreeLayout {
   int32_t nsplit_max, race_chunks;
-  size_t off_walk, off_count, off_claim, off_race_count, off_partials, off_cand, off_records, total;
+  size_t off_mail, off_count, off_race_count, off_partials, off_cand, total;
 };
+
+// Row chunks of a row: 16-byte vectors per row over vectors per chunk.
+template <typename Elem>
+static int32_t tree_nsplit(int32_t vocab) {
+  const int64_t nvec = vocab / Vec<Elem>::W;
+  return (int32_t)std::max<int64_t>(1, (nvec + kTreeNV * kRowThreads - 1) / (kTreeNV * kRowThreads));
+}
 
 static TreeLayout tree_layout(int32_t batch, int32_t vocab) {
   TreeLayout t;
-  const int64_t vec_f32 = vocab / 4;  // fp32 rows have the most 16-byte vectors
-  t.nsplit_max = (int32_t)std::max<int64_t>(1, (vec_f32 + kTreeNV * kRowThreads - 1) /
-                                                   (kTreeNV * kRowThreads));
+  t.nsplit_max = tree_nsplit<float>(vocab);  // fp32 rows have the most chunks
   constexpr int32_t kChunk = kRaceThreads * kTreeRaceTPT;
   t.race_chunks = (vocab + kChunk - 1) / kChunk;
-  const size_t B = (size_t)batch, L = kTreeMaxLayers;
-  t.off_walk = 0;
-  t.off_count = align_up(B * sizeof(unsigned long long));
-  t.off_claim = t.off_count + align_up(B * L * kTreeSlots * sizeof(uint32_t));
-  t.off_race_count = t.off_claim + align_up(B * L * sizeof(uint32_t));
+  const size_t B = (size_t)batch;
+  t.off_mail = 0;
+  t.off_count = align_up(B * kMailboxWords * sizeof(unsigned long long));
+  t.off_race_count = t.off_count + align_up(B * kTreeRows * sizeof(uint32_t));
   t.off_partials = t.off_race_count + align_up(B * sizeof(uint32_t));
-  t.off_cand = t.off_partials + align_up(B * L * kTreeSlots * (size_t)t.nsplit_max * sizeof(RowPartial));
-  t.off_records = t.off_cand + align_up(B * (size_t)t.race_chunks * sizeof(unsigned long long));
-  t.total = t.off_records + align_up(B * sizeof(ReqRecord));
+  t.off_cand = t.off_partials + align_up(B * kTreeRows * (size_t)t.nsplit_max * sizeof(RowPartial));
+  t.total = t.off_cand + align_up(B * (size_t)t.race_chunks * sizeof(unsigned long long));
   return t;
+}
+
+// Workgroups the device holds at once for the walk kernel (queried once per
+// device and element type).
+template <typename Elem>
+static int64_t tree_resident() {
+  static int64_t cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, tree_walk_kernel<Elem, kTreeNV>, kRowThreads, 0) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu < 1 ||
+        cus < 1)
+      return 256;
+    cached[dev] = (int64_t)per_cu * cus;
+  }
+  return cached[dev];
 }
 
 template <typename Elem>
@@ -704,25 +726,23 @@ static rs_status launch_tree(const void* logits, const int32_t* node_tokens, con
   a.max_nodes = max_nodes;
   a.max_depth = max_depth;
   a.V = V;
-  const int64_t nvec = V / Vec<Elem>::W;
-  a.nsplit = (int32_t)std::max<int64_t>(1, (nvec + kTreeNV * kRowThreads - 1) /
-                                               (kTreeNV * kRowThreads));
+  a.nsplit = tree_nsplit<Elem>(V);
   a.race_chunks = t.race_chunks;
+  // K workgroups per request, enough to fill the device once (any of a
+  // request's workgroups can take any of its chunks, so none waits on one
+  // that is not resident).
+  a.K = (int32_t)std::max<int64_t>(1, std::min<int64_t>(kTreeMaxK, tree_resident<Elem>() / B));
   a.out = out;
   a.path = path;
   a.nacc = nacc;
-  a.walk = reinterpret_cast<unsigned long long*>(w + t.off_walk);
+  a.mail = reinterpret_cast<unsigned long long*>(w + t.off_mail);
   a.count = reinterpret_cast<uint32_t*>(w + t.off_count);
-  a.claim = reinterpret_cast<uint32_t*>(w + t.off_claim);
   a.race_count = reinterpret_cast<uint32_t*>(w + t.off_race_count);
   a.partials = reinterpret_cast<RowPartial*>(w + t.off_partials);
   a.cand = reinterpret_cast<unsigned long long*>(w + t.off_cand);
-  a.records = reinterpret_cast<ReqRecord*>(w + t.off_records);
-  tree_init_kernel<<<(unsigned)B, 64, 0, stream>>>(node_tokens, node_parents, cu, N, max_nodes, max_depth, V,
-                                                         out, path, nacc, a.walk, a.count, a.claim, a.race_count);
+  tree_init_kernel<Elem><<<(unsigned)B, kRowThreads, 0, stream>>>(a);
   if (hipGetLastError() != hipSuccess) return RS_ERR_HIP;
-  const int64_t blocks = (int64_t)B * a.nsplit * (1 + (int64_t)kTreeSlots * max_depth) + (int64_t)B * a.race_chunks;
-  tree_walk_kernel<Elem, kTreeNV><<<(unsigned)blocks, kRowThreads, 0, stream>>>(a);
+  tree_walk_kernel<Elem, kTreeNV><<<(unsigned)((int64_t)B * a.K), kRowThreads, 0, stream>>>(a);
   return hipGetLastError() == hipSuccess ? RS_OK : RS_ERR_HIP;
 }
 
@@ -815,11 +835,9 @@ rs_status rs_verify_tree(const void* target_logits, rs_dtype logits_dtype, const
       ((uintptr_t)cu_num_nodes % 4) || ((uintptr_t)temperature % 4) || ((uintptr_t)output_token_ids % 4) ||
       ((uintptr_t)accepted_nodes % 4) || ((uintptr_t)num_accepted % 4))
     return RS_ERR_UNSUPPORTED;
-  // 1-D grid below 2^31 workgroups
+  // entry words hold a row's chunk count in 24 bits; the grid, B * K <= max(B, resident), stays below 2^31
   const rsv::TreeLayout t = rsv::tree_layout(batch, vocab);
-  if ((int64_t)batch * t.nsplit_max * (1 + (int64_t)rsv::kTreeSlots * max_depth) + (int64_t)batch * t.race_chunks >=
-      INT32_MAX)
-    return RS_ERR_UNSUPPORTED;
+  if (t.nsplit_max >= (1 << 24) || t.race_chunks >= (1 << 24)) return RS_ERR_UNSUPPORTED;
   if (!workspace || ((uintptr_t)workspace % 16) || workspace_bytes < t.total) return RS_ERR_WORKSPACE;
   if (logits_dtype == RS_BF16)
     return rsv::launch_tree<uint16_t>(target_logits, node_tokens, node_parents, cu_num_nodes, temperature, batch,

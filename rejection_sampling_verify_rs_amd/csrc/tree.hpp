@@ -24,30 +24,32 @@
 // one-child-per-node tree is the chain with one-hot q and uses the same
 // random numbers.
 //
-// Layout of the work (one launch, tree_walk_kernel, after tree_init_kernel).
-// Step d of a walk decides among the children of the node reached at step d
-// (the root at step 0) from that node's row.  The rows are streamed by walk
-// blocks in 16-vector chunks, ahead of the decisions that need them:
-//   layer 0: the root row.
-//   layer d >= 1: kTreeSpec speculative slots stream the rows of the first
-//     kTreeSpec children of the node reached at step d - 1 as soon as it is
-//     known (before step d - 1 picks one of them), and one on-demand slot
-//     streams the chosen child's row if it is not among them.
-//   race blocks, after the walk blocks: (request, 8192-token chunk) pairs
-//     that wait for their request's walk to stop and race their chunk of the
-//     stop row with the stop node's children masked out; the last one to
-//     arrive writes the extra token.
-// Step d is decided once both its node is known (step d - 1 decided) and that
-// node's row is complete: the step d - 1 decider, after publishing the node,
-// checks the row's chunk count; the row's last chunk, after counting itself,
-// checks the walk word.  Each stores, waits for the store, then loads, so at
-// least one of them sees both; a compare-and-swap on the step's claim word
-// lets exactly one decide.  A decider that finds the next row complete goes
-// on deciding, step after step.
-// A block only ever waits on blocks with smaller indices (earlier layers),
-// which were dispatched before it, and every wait is a bounded poll: a walk
-// that does not reach a block's step within the bound writes the request as
-// invalid (-1 row) instead of hanging.
+// Layout of the work: one launch (tree_walk_kernel, after tree_init_kernel)
+// of K workgroups per request.  Each request has
+// a list of entries that its workgroups work through in order:
+//   a row entry (node x, step d): stream the row of x (the root: -1) in
+//     chunks of 8 vectors per thread into that row's partial statistics;
+//   a race entry (stop node, step d): race the stop row in 8192-token chunks;
+//   an exit entry: the request is finished.
+// A workgroup claims chunks of the entry it is at from that entry's counter
+// (the first claim is made while the entry may still be unwritten), so a row
+// is streamed by many workgroups at once and a workgroup that is deciding
+// holds no chunk back.  The init kernel writes the
+// first entries: the root row and the rows of the first kTreeSpec children of
+// the root.  Step d's decider appends the next ones: when it accepts node x,
+// the row of x if it was not streamed ahead and the rows of the first
+// kTreeSpec children of x (needed one step later); when a random walk stops,
+// the race entry; when the request is finished, the exit entry.
+// A row's counter word holds its arrived chunks and a "chosen" bit that the
+// decider sets when it reaches the row's node.  Both sides update the word
+// with one atomic; the one whose update completes the pair (all chunks in and
+// chosen) decides the row's step, so exactly one does.  A decider that finds
+// the next row already complete goes on deciding, step after step.
+// Only a request's own workgroups touch its state, and no global counter is
+// updated.  A row entry the walk can no longer need (the walk stopped, or
+// reached another node at that step; the walk word only moves forward) is
+// skipped.  A workgroup waits only for its request's next entry, by a bounded
+// poll; a request that never finishes (not expected) keeps num_accepted = -1.
 #pragma once
 
 #include "common.hpp"
@@ -57,18 +59,29 @@
 
 namespace rsv {
 
-constexpr int kTreeMaxNodes = 64;  // one wavefront lane per node
-constexpr int kTreeRaceTPT = 32;   // tokens per thread of a race block (8192 tokens per chunk)
-constexpr int kTreeNV = 16;        // 16-byte vectors per thread of a walk block
-constexpr int kTreeMaxLayers = kTreeMaxNodes + 1;  // steps 0 .. max_depth, max_depth <= max_nodes
-constexpr int kTreeSpec = 4;                       // children rows streamed before their parent's step decides
-constexpr int kTreeSlots = kTreeSpec + 1;          // plus one on-demand slot per layer
-constexpr int32_t kTreePollLimit = 1 << 17;        // polls (about 1 us each) before a block gives up
+constexpr int kTreeMaxNodes = 64;               // one wavefront lane per node
+constexpr int kTreeRows = kTreeMaxNodes + 1;    // the root row and one per node
+constexpr int kTreeEntries = kTreeRows + 2;     // every row at most once, the race, the exit
+constexpr int kTreeRaceTPT = 32;                // tokens per thread of a race chunk (8192 per chunk)
+constexpr int kTreeNV = 8;                      // 16-byte vectors per thread of a row chunk
+constexpr int kTreeSpec = 1;                    // children rows streamed before their parent is reached
+constexpr int32_t kTreeMaxK = 64;               // workgroups per request, at most
+constexpr int32_t kTreePollLimit = 1 << 18;     // polls before a workgroup stops waiting for an entry
+constexpr uint32_t kChosen = 0x80000000u;       // row counter: the row's node was reached
+// Per-request mailbox of 2 KiB, the words a request's workgroups poll and
+// update: the walk word (byte 0), the entry tail (byte 8), the entries (from
+// byte 128) and the entries' chunk claims (from byte 1024).  Each request's
+// words sit on lines of their own, away from other requests'.
+constexpr int kMailboxWords = 256;   // 8-byte words per mailbox
+constexpr int kMailboxEntries = 16;  // first entry word
+constexpr int kMailboxClaims = 128;  // first word of the 32-bit claim counters
+static_assert(kMailboxEntries + kTreeEntries <= kMailboxClaims, "entries fit the mailbox");
+static_assert(kMailboxClaims + (kTreeEntries + 1) / 2 <= kMailboxWords, "claims fit the mailbox");
 
 // Walk word of a request: step (bits 0-7), node + 1 (bits 8-15), status
-// (bits 16-23).  Walking: the row of `node` is streamed at `step`.  Stopped:
-// the walk ended at `step` on `node`, whose row is raced.  Done: the output
-// row is written (greedy stop).  Invalid: -1 row written.
+// (bits 16-23).  Walking: step `step` decides among the children of `node`.
+// Stopped: the walk ended at `step` on `node`, whose row is being raced.
+// Done: the output row is written.  Invalid: -1 row written by the init kernel.
 constexpr uint32_t kWalking = 1, kStopped = 2, kWalkDone = 3, kWalkInvalid = 4;
 __device__ __forceinline__ unsigned long long walk_word(uint32_t step, int32_t node, uint32_t status) {
   return (unsigned long long)step | ((unsigned long long)(uint32_t)(node + 1) << 8) | ((unsigned long long)status << 16);
@@ -76,6 +89,50 @@ __device__ __forceinline__ unsigned long long walk_word(uint32_t step, int32_t n
 __device__ __forceinline__ uint32_t walk_step(unsigned long long w) { return (uint32_t)(w & 0xFF); }
 __device__ __forceinline__ int32_t walk_node(unsigned long long w) { return (int32_t)((w >> 8) & 0xFF) - 1; }
 __device__ __forceinline__ uint32_t walk_status(unsigned long long w) { return (uint32_t)((w >> 16) & 0xFF); }
+
+// Entry word: node + 1 (bits 0-7), step (8-15), chunks (16-39), kind
+// (40-41), bit 63 set (a zero word is an entry not yet written).
+constexpr uint32_t kEntryRow = 0, kEntryRace = 1, kEntryExit = 2;
+__device__ __forceinline__ unsigned long long entry_word(uint32_t kind, int32_t node, int32_t d, int32_t chunks) {
+  return (1ull << 63) | ((unsigned long long)kind << 40) | ((unsigned long long)(uint32_t)chunks << 16) |
+         ((unsigned long long)(uint32_t)d << 8) | (uint32_t)(node + 1);
+}
+__device__ __forceinline__ int32_t entry_node(unsigned long long e) { return (int32_t)(e & 0xFF) - 1; }
+__device__ __forceinline__ int32_t entry_step(unsigned long long e) { return (int32_t)((e >> 8) & 0xFF); }
+__device__ __forceinline__ int32_t entry_chunks(unsigned long long e) { return (int32_t)((e >> 16) & 0xFFFFFF); }
+__device__ __forceinline__ uint32_t entry_kind(unsigned long long e) { return (uint32_t)((e >> 40) & 3u); }
+
+template <typename Args>
+__device__ __forceinline__ unsigned long long* walk_of(const Args& a, int32_t b) {
+  return a.mail + (int64_t)b * kMailboxWords;
+}
+template <typename Args>
+__device__ __forceinline__ uint32_t* tail_of(const Args& a, int32_t b) {
+  return reinterpret_cast<uint32_t*>(a.mail + (int64_t)b * kMailboxWords + 1);
+}
+template <typename Args>
+__device__ __forceinline__ unsigned long long* entries_of(const Args& a, int32_t b) {
+  return a.mail + (int64_t)b * kMailboxWords + kMailboxEntries;
+}
+template <typename Args>
+__device__ __forceinline__ uint32_t* claims_of(const Args& a, int32_t b) {
+  return reinterpret_cast<uint32_t*>(a.mail + (int64_t)b * kMailboxWords + kMailboxClaims);
+}
+
+// Lane k's value to every lane (k wavefront-uniform).
+__device__ __forceinline__ int32_t lane_i32(int32_t v, int32_t k) { return __builtin_amdgcn_readlane(v, k); }
+__device__ __forceinline__ double lane_f64(double v, int32_t k) {
+  const unsigned long long x = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int32_t)(uint32_t)x, k);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int32_t)(uint32_t)(x >> 32), k);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// Index of the i-th set bit of m (-1: fewer than i + 1 bits).
+__device__ __forceinline__ int32_t nth_bit(unsigned long long m, int32_t i) {
+  for (int32_t k = 0; k < i && m; ++k) m &= m - 1ull;
+  return m ? __ffsll((long long)m) - 1 : -1;
+}
 
 template <typename Elem>
 struct TreeArgs {
@@ -86,118 +143,164 @@ struct TreeArgs {
   const float* temperature;
   uint64_t seed;
   int32_t B, N, max_nodes, max_depth, V;
-  int32_t nsplit;       // chunks per row of a walk block
-  int32_t race_chunks;  // race blocks per request
-  int32_t* out;         // [B, max_depth + 1]
-  int32_t* path;        // [B, max_depth]
-  int32_t* nacc;        // [B]
-  unsigned long long* walk;  // [B]
-  uint32_t* count;           // [B * (max_depth + 1) * kTreeSlots] chunk arrivals per (step, slot)
-  uint32_t* claim;           // [B * (max_depth + 1)] a step's decision claimed
-  uint32_t* race_count;      // [B] race chunk arrivals
-  RowPartial* partials;      // [B * (max_depth + 1) * kTreeSlots * nsplit]
-  unsigned long long* cand;  // [B * race_chunks] packed race winners
-  ReqRecord* records;        // [B] the stop row's race
+  int32_t nsplit;        // row chunks per row
+  int32_t race_chunks;   // race chunks per row
+  int32_t K;             // workgroups per request
+  int32_t* out;          // [B, max_depth + 1]
+  int32_t* path;         // [B, max_depth]
+  int32_t* nacc;         // [B]
+  unsigned long long* mail;     // [B * kMailboxWords] walk word, entry tail, entries
+  uint32_t* count;              // [B * kTreeRows] arrived chunks | kChosen, per row
+  uint32_t* race_count;         // [B] arrived race chunks
+  RowPartial* partials;         // [B * kTreeRows * nsplit]
+  unsigned long long* cand;     // [B * race_chunks] packed race winners
 };
 
-// One wavefront per request: validates the tree (sizes, parents before
-// children, tokens in range, every node shallower than max_depth), writes -1
-// rows for an invalid one, clears the request's counters and starts its walk.
-__global__ __launch_bounds__(64) void tree_init_kernel(const int32_t* __restrict__ tokens,
-                                                       const int32_t* __restrict__ parents,
-                                                       const int32_t* __restrict__ cu, int32_t N, int32_t max_nodes,
-                                                       int32_t max_depth, int32_t V, int32_t* __restrict__ out,
-                                                       int32_t* __restrict__ path, int32_t* __restrict__ nacc,
-                                                       unsigned long long* __restrict__ walk,
-                                                       uint32_t* __restrict__ count, uint32_t* __restrict__ claim,
-                                                       uint32_t* __restrict__ race_count) {
-  const int32_t b = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int32_t s = cu[b], e = cu[b + 1];
-  const int32_t n = e - s;
-  bool ok = s >= 0 && s <= e && e <= N && n <= max_nodes;
-  int32_t tk = 0, pr = -1;
-  if (ok && lane < n) {
-    tk = tokens[s + lane];
-    pr = parents[s + lane];
-  }
-  ok = ok && __ballot(lane < n && (pr < -1 || pr >= lane || tk < 0 || tk >= V)) == 0ull;
-  int32_t dep = 0;  // depth of node lane: a parent's depth is final after (its depth + 1) rounds
-  for (int32_t r = 0; ok && r < n; ++r) {
-    const int32_t dp = __shfl(dep, pr < 0 ? lane : pr);
-    dep = pr < 0 ? 0 : dp + 1;
-  }
-  ok = ok && __ballot(lane < n && dep >= max_depth) == 0ull;
-  for (int32_t i = lane; i < (max_depth + 1) * kTreeSlots; i += 64)
-    count[(int64_t)b * (max_depth + 1) * kTreeSlots + i] = 0u;
-  for (int32_t d = lane; d <= max_depth; d += 64) claim[(int64_t)b * (max_depth + 1) + d] = 0u;
-  if (lane == 0) {
-    race_count[b] = 0u;
-    walk[b] = ok ? walk_word(0, -1, kWalking) : walk_word(0, -1, kWalkInvalid);
-  }
-  if (!ok) {
-    for (int32_t i = lane; i <= max_depth; i += 64) out[(int64_t)b * (max_depth + 1) + i] = -1;
-    for (int32_t i = lane; i < max_depth; i += 64) path[(int64_t)b * max_depth + i] = -1;
-    if (lane == 0) nacc[b] = -1;
-  }
-}
-
-// Gives up on a request whose walk did not progress within the poll bound
-// (never expected: the blocks waited on were dispatched earlier): -1 row.
+// One workgroup per request: validates the tree (sizes, parents before
+// children, tokens in range, every node shallower than max_depth), fills the
+// request's output rows with -1 (a valid walk overwrites them as it goes),
+// clears its counters and writes its first entries: the root row and the
+// rows of the root's first children, with the root row chosen; an invalid
+// request gets only the exit entry.
 template <typename Elem>
-__device__ __forceinline__ void tree_give_up(const TreeArgs<Elem>& a, int32_t b) {
-  const int lane = threadIdx.x & 63;
-  for (int32_t i = lane; i <= a.max_depth; i += 64) a.out[(int64_t)b * (a.max_depth + 1) + i] = -1;
-  for (int32_t i = lane; i < a.max_depth; i += 64) a.path[(int64_t)b * a.max_depth + i] = -1;
-  if (lane == 0) a.nacc[b] = -1;
-}
-
-// Thread 0 polls the walk word of request b until `ready` holds; every thread
-// gets the word (0 when the bound expired).
-template <typename Ready>
-__device__ __forceinline__ unsigned long long tree_wait(const unsigned long long* walk, int32_t b,
-                                                        unsigned long long* s_w, Ready ready) {
-  if (threadIdx.x == 0) {
-    unsigned long long w = load_coherent(walk + b);
-    int32_t i = 0;
-    for (; !ready(w) && i < kTreePollLimit; ++i) {
-      __builtin_amdgcn_s_sleep(2);
-      w = load_coherent(walk + b);
+__global__ __launch_bounds__(kRowThreads) void tree_init_kernel(TreeArgs<Elem> a) {
+  __shared__ int s_ok;
+  __shared__ unsigned long long s_kids;
+  const int32_t b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < 64) {
+    const int32_t s = a.cu[b], e = a.cu[b + 1];
+    const int32_t n = e - s;
+    bool ok = s >= 0 && s <= e && e <= a.N && n <= a.max_nodes;
+    int32_t tk = 0, pr = -1;
+    if (ok && lane < n) {
+      tk = a.tokens[s + lane];
+      pr = a.parents[s + lane];
     }
-    *s_w = ready(w) ? w : 0ull;
+    ok = ok && __ballot(lane < n && (pr < -1 || pr >= lane || tk < 0 || tk >= a.V)) == 0ull;
+    int32_t dep = 0;  // depth of node lane: a parent's depth is final after (its depth + 1) rounds
+    for (int32_t r = 0; ok && r < n; ++r) {
+      const int32_t dp = __shfl(dep, pr < 0 ? lane : pr);
+      dep = pr < 0 ? 0 : dp + 1;
+    }
+    ok = ok && __ballot(lane < n && dep >= a.max_depth) == 0ull;
+    const unsigned long long kids = __ballot(ok && lane < n && pr == -1);
+    if (tid == 0) {
+      s_ok = ok;
+      s_kids = kids;
+    }
   }
   __syncthreads();
-  const unsigned long long w = *s_w;
-  __syncthreads();  // s_w is reused
-  return w;
-}
-
-__device__ __forceinline__ int64_t tree_slot_index(int32_t b, int32_t max_depth, int32_t d, int32_t slot) {
-  return ((int64_t)b * (max_depth + 1) + d) * kTreeSlots + slot;
+  const bool ok = s_ok;
+  const unsigned long long kids = s_kids;
+  const int32_t nspec = ok ? min(__popcll(kids), kTreeSpec) : 0;
+  unsigned long long* E = entries_of(a, b);
+  for (int32_t i = tid; i < kTreeEntries; i += kRowThreads) {
+    unsigned long long w = 0ull;
+    if (!ok)
+      w = i == 0 ? entry_word(kEntryExit, -1, 0, 0) : 0ull;
+    else if (i == 0)
+      w = entry_word(kEntryRow, -1, 0, a.nsplit);
+    else if (i <= nspec)
+      w = entry_word(kEntryRow, nth_bit(kids, i - 1), 1, a.nsplit);
+    E[i] = w;
+  }
+  for (int32_t i = tid; i < kTreeRows; i += kRowThreads)
+    a.count[(int64_t)b * kTreeRows + i] = (i == 0 && ok) ? kChosen : 0u;
+  for (int32_t i = tid; i < kTreeEntries; i += kRowThreads) claims_of(a, b)[i] = 0u;
+  for (int32_t i = tid; i <= a.max_depth; i += kRowThreads) a.out[(int64_t)b * (a.max_depth + 1) + i] = -1;
+  for (int32_t i = tid; i < a.max_depth; i += kRowThreads) a.path[(int64_t)b * a.max_depth + i] = -1;
+  if (tid == 0) {
+    a.nacc[b] = -1;
+    a.race_count[b] = 0u;
+    *tail_of(a, b) = ok ? (uint32_t)(1 + nspec) : 1u;
+    *walk_of(a, b) = ok ? walk_word(0, -1, kWalking) : walk_word(0, -1, kWalkInvalid);
+  }
 }
 
 // Rank of node x among the children of its parent (lanes hold the nodes'
-// parents), and the node of rank i among the children of `cur` (-1: none).
+// parents).
 __device__ __forceinline__ int32_t child_rank(int32_t par, int32_t n, int32_t x) {
   const int lane = threadIdx.x & 63;
-  const int32_t px = __shfl(par, x);
+  const int32_t px = lane_i32(par, x);
   const unsigned long long sib = __ballot(lane < n && par == px);
   return __popcll(sib & ((1ull << x) - 1ull));
 }
-__device__ __forceinline__ int32_t nth_child(int32_t par, int32_t n, int32_t cur, int32_t i) {
-  const int lane = threadIdx.x & 63;
-  unsigned long long kids = __ballot(lane < n && par == cur);
-  for (int32_t k = 0; k < i && kids; ++k) kids &= kids - 1ull;
-  return kids ? __ffsll((long long)kids) - 1 : -1;
+
+__device__ __forceinline__ RowPartial* tree_partials(RowPartial* p, int32_t b, int32_t x, int32_t nsplit) {
+  return p + ((int64_t)b * kTreeRows + x + 1) * nsplit;
 }
 
-// Decisions of request b from step d on (wavefront 0 of the block that
-// claimed step d): merge the row's partial statistics, choose the child or
-// stop, write the step's output and publish the walk word; while the next
-// step's row is already complete, claim and decide it too.
+// A row's statistics from its chunk partials, one wavefront: random rows
+// get the common shift (largest chunk shift) and the fp64 sum rescaled to it,
+// summed in chunk order; greedy rows the largest value, lowest index on ties.
+// The chunks' partials are loaded across lanes and folded through lane reads
+// (a short scalar loop, no shuffle chain).  The decider and the race chunks
+// call it on the same partials and so get the same numbers.
+__device__ __forceinline__ void tree_merge(const RowPartial* P, int32_t nsplit, bool greedy, float& shift,
+                                           double& S, int32_t& amax) {
+  const int lane = threadIdx.x & 63;
+  float sh = -INFINITY;
+  double acc = 0.0;
+  float m = -INFINITY;
+  int32_t idx = INT_MAX;
+  for (int32_t c0 = 0; c0 < nsplit; c0 += 64) {
+    const int32_t nc = min(64, nsplit - c0);
+    RowPartial r;
+    r.shift = -INFINITY;
+    r.argmax = -1;
+    r.sum = 0.0;
+    if (lane < nc) r = load_partial<true>(P + c0 + lane);
+    if (greedy) {
+      for (int32_t c = 0; c < nc; ++c) {
+        const int32_t ac = lane_i32(r.argmax, c);
+        const float mc = __int_as_float(lane_i32(__float_as_int(r.shift), c));
+        if (ac >= 0 && (mc > m || (mc == m && ac < idx))) {
+          m = mc;
+          idx = ac;
+        }
+      }
+      continue;
+    }
+    float shc = -INFINITY;  // this batch's shift, then the running one
+    for (int32_t c = 0; c < nc; ++c) shc = fmaxf(shc, __int_as_float(lane_i32(__float_as_int(r.shift), c)));
+    if (shc > sh) {  // rescale what was summed so far
+      if (acc > 0.0) acc *= exp2((double)sh - (double)shc);
+      sh = shc;
+    }
+    const double t = r.sum > 0.0 ? r.sum * exp2((double)r.shift - (double)sh) : 0.0;
+    for (int32_t c = 0; c < nc; ++c) acc += lane_f64(t, c);
+  }
+  if (greedy) {
+    amax = idx == INT_MAX ? -1 : idx;
+    return;
+  }
+  shift = sh;
+  S = acc;
+}
+
+// Appends one entry to request b's list (one wavefront, lane 0).
 template <typename Elem>
-__device__ __forceinline__ void tree_decide(const TreeArgs<Elem>& a, int32_t b, int32_t d, int32_t cur, int32_t slot,
-                                            int32_t s, int32_t n, float T, int32_t tok, int32_t par) {
+__device__ __forceinline__ void tree_append(const TreeArgs<Elem>& a, int32_t b, unsigned long long e) {
+  if ((threadIdx.x & 63) != 0) return;
+  const uint32_t r = __hip_atomic_fetch_add(tail_of(a, b), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (r < (uint32_t)kTreeEntries) store_coherent(entries_of(a, b) + r, e);
+}
+
+// Marks request b finished (one wavefront; its output row is written).
+template <typename Elem>
+__device__ __forceinline__ void tree_finish(const TreeArgs<Elem>& a, int32_t b, int32_t d, int32_t cur) {
+  if ((threadIdx.x & 63) == 0) store_coherent(walk_of(a, b), walk_word((uint32_t)d, cur, kWalkDone));
+  tree_append(a, b, entry_word(kEntryExit, -1, 0, 0));
+}
+
+// Decisions of request b from step d on (wavefront 0 of the workgroup that
+// completed the pair for step d): merge the row's partials, choose the child
+// or stop, write the step's output and append the entries that come next;
+// while the next row is already complete, decide it too.
+template <typename Elem>
+__device__ __forceinline__ void tree_decide(const TreeArgs<Elem>& a, int32_t b, int32_t d, int32_t cur, int32_t s,
+                                            int32_t n, float T, int32_t tok, int32_t par) {
   const int lane = threadIdx.x & 63;
   const bool greedy = !(T > 0.f);
   const float cs = greedy ? 0.f : scale_of(T);
@@ -209,206 +312,143 @@ __device__ __forceinline__ void tree_decide(const TreeArgs<Elem>& a, int32_t b, 
     const bool child = lane < n && par == cur;
     // the children's logits and the partials are loaded together
     const float lt = (!greedy && child) ? to_f32(prow[tok]) : -INFINITY;
-    const RowPartial* P = a.partials + tree_slot_index(b, a.max_depth, d, slot) * a.nsplit;
     float shift = -INFINITY;
     double S = 0.0;
     int32_t amax = -1, next = -1;
+    tree_merge(tree_partials(a.partials, b, cur, a.nsplit), a.nsplit, greedy, shift, S, amax);
     if (greedy) {
-      amax = merge_greedy<true>(P, a.nsplit);
       const unsigned long long m = __ballot(child && tok == amax);
       next = m ? __ffsll((long long)m) - 1 : -1;
     } else {
-      merge_random<true>(P, a.nsplit, shift, S);
       const unsigned long long kids = __ballot(child);
       bool dup = false;  // a repeat of an earlier sibling's token
-      for (int k = 0; k < 63; ++k) {
-        const int32_t tk = __shfl(tok, k);
-        dup = dup || (k < lane && ((kids >> k) & 1ull) && tk == tok);
+      for (unsigned long long m = kids; m; m &= m - 1ull) {
+        const int32_t k = __ffsll((long long)m) - 1;
+        dup = dup || (k < lane && lane_i32(tok, k) == tok);
       }
-      const bool take = child && !dup;
-      double cum = take ? exp2((double)lt * (double)cs - (double)shift) / S : 0.0;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {  // inclusive prefix sum in node order
-        const double v = __shfl_up(cum, o);
-        if (lane >= o) cum += v;
-      }
+      const unsigned long long take = __ballot(child && !dup);
+      const double pk = exp2((double)lt * (double)cs - (double)shift) / S;
+      // the siblings in node order, each adding its p to the accumulated sum
       const double u = accept_uniform(a.seed, b, d);
-      const unsigned long long m = __ballot(take && u < cum);
-      next = m ? __ffsll((long long)m) - 1 : -1;
+      double cum = 0.0;
+      for (unsigned long long m = take; m; m &= m - 1ull) {
+        const int32_t k = __ffsll((long long)m) - 1;
+        cum += lane_f64(pk, k);
+        if (u < cum) {
+          next = k;
+          break;
+        }
+      }
     }
     if (next < 0) {  // stop at step d
-      for (int32_t i = d + lane; i < a.max_depth; i += 64) pb[i] = -1;
-      for (int32_t i = d + 1 + lane; i <= a.max_depth; i += 64) ob[i] = -1;
       if (greedy) {
         if (lane == 0) {
           ob[d] = amax;
           a.nacc[b] = d;
-          store_coherent(a.walk + b, walk_word((uint32_t)d, cur, kWalkDone));
         }
+        tree_finish(a, b, d, cur);
         return;
       }
-      if (lane == 0) {  // the race over p without the stop node's children, by the race blocks
-        ReqRecord r;
-        r.mode = kModeBonus;
-        r.phase = 0;
-        r.n = d;
-        r.row = (int32_t)row;
-        r.slot0 = s;
-        r.exclude = cur;  // the stop node (-1: the root); its children leave the race
-        r.c = cs;
-        r.shift = shift;
-        r.inv_sum = (float)(1.0 / S);
-        r.tau = -INFINITY;
-        r.pad[0] = n;
-        r.pad[1] = 0;
-        unsigned long long w[sizeof(ReqRecord) / 8];
-        __builtin_memcpy(w, &r, sizeof(ReqRecord));
-#pragma unroll
-        for (int i = 0; i < (int)(sizeof(ReqRecord) / 8); ++i)
-          store_coherent(reinterpret_cast<unsigned long long*>(a.records + b) + i, w[i]);
-        wait_memory();  // the record is visible before the walk word says "stopped"
-        store_coherent(a.walk + b, walk_word((uint32_t)d, cur, kStopped));
-      }
+      // the extra token: the race over p without the stop node's children
+      if (lane == 0) store_coherent(walk_of(a, b), walk_word((uint32_t)d, cur, kStopped));
+      tree_append(a, b, entry_word(kEntryRace, cur, d, a.race_chunks));
       return;
     }
     // descend: the accepted node is emitted, and step d + 1 decides among its children
-    const int32_t ntok = __shfl(tok, next);
+    const int32_t ntok = lane_i32(tok, next);
     const int32_t rank = child_rank(par, n, next);
-    int go = 0;
+    const unsigned long long spec = __ballot(lane < n && par == next);  // next's children, the first few streamed now
+    const int32_t nspec = min(__popcll(spec), kTreeSpec);
+    const int32_t own = rank >= kTreeSpec ? 1 : 0;  // next's row was not streamed ahead
+    const int32_t nent = own + nspec;
+    uint32_t base = 0u, old = 0u;
     if (lane == 0) {
       ob[d] = ntok;
       pb[d] = next;
-      store_coherent(a.walk + b, walk_word((uint32_t)d + 1, next, kWalking));
-      wait_memory();  // published before the next row's count is read
-      if (rank < kTreeSpec &&
-          __hip_atomic_load(a.count + tree_slot_index(b, a.max_depth, d + 1, rank), __ATOMIC_RELAXED,
-                            __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)a.nsplit)
-        go = atomic_cas32(reinterpret_cast<int32_t*>(a.claim) + (int64_t)b * (a.max_depth + 1) + d + 1, 0, 1);
+      store_coherent(walk_of(a, b), walk_word((uint32_t)d + 1, next, kWalking));
+      if (nent > 0) base = __hip_atomic_fetch_add(tail_of(a, b), (uint32_t)nent, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (!__shfl(go, 0)) return;
+    if (lane == 1)  // next is reached: its row's last chunk, or this decider, decides step d + 1
+      old = __hip_atomic_fetch_or(a.count + (int64_t)b * kTreeRows + next + 1, kChosen, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+    base = (uint32_t)lane_i32((int32_t)base, 0);
+    old = (uint32_t)lane_i32((int32_t)old, 1);
+    if (lane < nent && base + lane < (uint32_t)kTreeEntries) {
+      const int32_t x = lane < own ? next : nth_bit(spec, lane - own);
+      store_coherent(entries_of(a, b) + base + lane,
+                     entry_word(kEntryRow, x, x == next ? d + 1 : d + 2, a.nsplit));
+    }
+    if (old != (uint32_t)a.nsplit) return;  // the row is still streaming
     ++d;
     cur = next;
-    slot = rank;
   }
 }
 
-// Walk block: chunk c of the row in slot `slot` of layer d of request b (see
-// the layout above).
+// Row chunk c of the row of node x (root: -1), decided at step d.
 template <typename Elem, int NV>
-__device__ __forceinline__ void tree_walk_block(const TreeArgs<Elem>& a, int32_t d, int32_t b, int32_t slot,
-                                                int32_t c, unsigned long long* s_w) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  // Layer 0 streams the root row at once; a speculative slot waits for the
-  // node of step d - 1, the on-demand slot for the node of step d.
-  const uint32_t need = slot < kTreeSpec ? (uint32_t)(d > 0 ? d - 1 : 0) : (uint32_t)d;
-  unsigned long long w;
-  if (d > 0) {
-    w = tree_wait(a.walk, b, s_w, [need](unsigned long long v) {
-      return walk_status(v) != kWalking || walk_step(v) >= need;
-    });
-    if (w == 0ull) {  // gave up: the walk never reached the step
-      if (tid < 64) tree_give_up(a, b);
-      return;
-    }
-  } else {
-    if (tid == 0) *s_w = load_coherent(a.walk + b);
-    __syncthreads();
-    w = *s_w;
-    __syncthreads();
-  }
-  if (walk_status(w) != kWalking) return;  // ended, or invalid (never streamed)
-  // The request's nodes, lane i = node i, in every wavefront (each computes
-  // the same row to stream; wavefront 0 also takes the decisions).  The init
-  // kernel validated the tree.
-  const int32_t s = a.cu[b], n = a.cu[b + 1] - s;
-  int32_t tok = 0, par = -2;
-  if (lane < n) {
-    tok = a.tokens[s + lane];
-    par = a.parents[s + lane];
-  }
-  const uint32_t step = walk_step(w);
-  int32_t node;
-  if (d == 0) {
-    node = -1;
-  } else if (slot < kTreeSpec) {
-    if (step > (uint32_t)d) return;  // step d already decided: its row was complete
-    // the slot-th child of the node of step d - 1: the current node, or, once
-    // step d - 1 is decided, the parent of the current node
-    int32_t prev = walk_node(w);
-    if (step == (uint32_t)d) prev = __shfl(par, prev);
-    node = nth_child(par, n, prev, slot);
-    if (node < 0 || (step == (uint32_t)d && node != walk_node(w))) return;  // no such child / not the chosen one
-  } else {
-    if (step != (uint32_t)d) return;
-    node = walk_node(w);
-    if (child_rank(par, n, node) < kTreeSpec) return;  // a speculative slot streams it
-  }
-  const float T = a.temperature[b];
-  const int64_t row = (int64_t)s + b + 1 + node;
-  chunk_task<Elem, NV, true>(a.logits, nullptr, row, T, a.V, a.nsplit, c, -1, 0,
-                             a.partials + tree_slot_index(b, a.max_depth, d, slot) * a.nsplit, nullptr);
+__device__ __forceinline__ void tree_row_chunk(const TreeArgs<Elem>& a, int32_t b, int32_t d, int32_t x, int32_t c,
+                                               int32_t s, int32_t n, float T, int32_t tok, int32_t par,
+                                               uint32_t* claim, uint32_t* s_c) {
+  const int tid = threadIdx.x;
+  chunk_task<Elem, NV, true>(a.logits, nullptr, (int64_t)s + b + 1 + x, T, a.V, a.nsplit, c, -1, 0,
+                             tree_partials(a.partials, b, x, a.nsplit), nullptr);
   if (tid >= 64) return;
   int go = 0;
   if (tid == 0) {
     wait_memory();  // the partial is visible before it is counted
-    if (arrive_last(a.count + tree_slot_index(b, a.max_depth, d, slot), (uint32_t)a.nsplit)) {
-      // the row is complete: decide step d if its node is this row's
-      const unsigned long long v = load_coherent(a.walk + b);
-      if (walk_status(v) == kWalking && walk_step(v) == (uint32_t)d && walk_node(v) == node)
-        go = atomic_cas32(reinterpret_cast<int32_t*>(a.claim) + (int64_t)b * (a.max_depth + 1) + d, 0, 1);
-    }
+    const uint32_t old = __hip_atomic_fetch_add(a.count + (int64_t)b * kTreeRows + x + 1, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    *s_c = __hip_atomic_fetch_add(claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    go = old == (kChosen | (uint32_t)(a.nsplit - 1));
   }
-  if (__shfl(go, 0)) tree_decide(a, b, d, node, slot, s, n, T, tok, par);
+  if (lane_i32(go, 0)) tree_decide(a, b, d, x, s, n, T, tok, par);
 }
 
-// Race block: chunk rc (kRaceThreads * kTreeRaceTPT tokens) of request b's
-// stop row, the stop node's children (those with a token in the chunk)
-// marked in an LDS bitmap and given weight 0.  The last chunk to arrive
-// writes the extra token; if every token with mass was a child of the stop
-// node it races over p instead.
+// Race chunk rc (kRaceThreads * kTreeRaceTPT tokens) of request b's stop row
+// (node cur, step d), the stop node's children (those with a token in the
+// chunk) marked in an LDS bitmap and given weight 0.  The row's statistics
+// are merged at a workgroup's first chunk of the entry (`merged`) and kept.
+// The last chunk to arrive writes the extra token; if every token with mass
+// was a child of the stop node it races over p instead.
 template <typename Elem>
-__device__ __forceinline__ void tree_race_block(const TreeArgs<Elem>& a, int32_t b, int32_t rc,
-                                                unsigned long long* s_w) {
+__device__ __forceinline__ void tree_race_chunk(const TreeArgs<Elem>& a, int32_t b, int32_t d, int32_t cur,
+                                                int32_t rc, int32_t s, int32_t n, float T, int32_t tok, int32_t par,
+                                                bool& merged, float& shift, float& inv_sum, uint32_t* claim,
+                                                uint32_t* s_c) {
   constexpr int NG = kTreeRaceTPT / 4;  // groups of four tokens per thread
   constexpr int kChunk = kRaceThreads * kTreeRaceTPT;
   using R4 = Raw4<Elem>;
   __shared__ uint32_t bits[kChunk / 32];
   __shared__ unsigned long long lds_u[kRaceThreads / 64];
-  const int tid = threadIdx.x;
-  const unsigned long long w =
-      tree_wait(a.walk, b, s_w, [](unsigned long long v) { return walk_status(v) != kWalking; });
-  if (w == 0ull) {
-    if (tid < 64) tree_give_up(a, b);
-    return;
-  }
-  if (walk_status(w) != kStopped) return;  // greedy, invalid, or done
-  ReqRecord rec;
-  {
-    unsigned long long r[sizeof(ReqRecord) / 8];
-#pragma unroll
-    for (int i = 0; i < (int)(sizeof(ReqRecord) / 8); ++i)
-      r[i] = load_coherent(reinterpret_cast<const unsigned long long*>(a.records + b) + i);
-    __builtin_memcpy(&rec, r, sizeof(ReqRecord));
-  }
-  const int32_t x0 = rc * kChunk;
-  for (int i = tid; i < kChunk / 32; i += kRaceThreads) bits[i] = 0u;
-  __syncthreads();
-  if (tid < rec.pad[0] && a.parents[rec.slot0 + tid] == rec.exclude) {
-    const int32_t x = a.tokens[rec.slot0 + tid] - x0;
-    if (x >= 0 && x < kChunk) atomicOr(bits + (x >> 5), 1u << (x & 31));
-  }
-  __syncthreads();
-  const Elem* lrow = a.logits + (int64_t)rec.row * a.V;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t row = (int64_t)s + b + 1 + cur;
+  const float cs = scale_of(T);
+  const Elem* lrow = a.logits + row * a.V;
   const bool fast = ((uintptr_t)lrow % sizeof(typename R4::T)) == 0;
   const int32_t Gend = (a.V + 3) / 4, Gfull = fast ? a.V / 4 : 0;
   const int32_t G0 = rc * (kRaceThreads * NG);
-  const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
   typename R4::T lw[NG];
   if (Gfull > 0) {  // unconditional loads (index clamped into the vector part): all in flight together
 #pragma unroll
     for (int i = 0; i < NG; ++i)
       lw[i] = reinterpret_cast<const typename R4::T*>(lrow)[min(G0 + tid + i * kRaceThreads, Gfull - 1)];
   }
+  if (!merged) {  // while the chunk's loads are in flight
+    double S = 0.0;
+    int32_t amax = -1;
+    tree_merge(tree_partials(a.partials, b, cur, a.nsplit), a.nsplit, false, shift, S, amax);
+    inv_sum = (float)(1.0 / S);
+    merged = true;
+  }
+  const int32_t x0 = rc * kChunk;
+  for (int i = tid; i < kChunk / 32; i += kRaceThreads) bits[i] = 0u;
+  __syncthreads();
+  if (tid < 64 && lane < n && par == cur) {  // wavefront 0 holds the nodes
+    const int32_t x = tok - x0;
+    if (x >= 0 && x < kChunk) atomicOr(bits + (x >> 5), 1u << (x & 31));
+  }
+  __syncthreads();
+  const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
   float best_key = 0.f;
   int32_t best_x = INT_MAX;
   const float qz[4] = {0.f, 0.f, 0.f, 0.f};
@@ -427,8 +467,8 @@ __device__ __forceinline__ void tree_race_block(const TreeArgs<Elem>& a, int32_t
     const uint32_t mb = bits[xl >> 5] >> (xl & 31);
 #pragma unroll
     for (int k = 0; k < 4; ++k) l[k] = ((mb >> k) & 1u) ? -INFINITY : l[k];
-    race_group_m<kModeBonus, false>(l, qz, -1, rec.c, rec.shift, rec.inv_sum, -INFINITY, k0, k1, (uint32_t)rec.n,
-                                    (uint32_t)b, G, best_key, best_x);
+    race_group_m<kModeBonus, false>(l, qz, -1, cs, shift, inv_sum, -INFINITY, k0, k1, (uint32_t)d, (uint32_t)b, G,
+                                    best_key, best_x);
   }
   const unsigned long long win = block_reduce<kRaceThreads>(pack_key(best_key, best_x), lds_u, MaxOp());
   if (tid >= 64) return;
@@ -437,10 +477,11 @@ __device__ __forceinline__ void tree_race_block(const TreeArgs<Elem>& a, int32_t
     store_coherent(a.cand + (int64_t)b * a.race_chunks + rc, win);
     wait_memory();
     last = arrive_last(a.race_count + b, (uint32_t)a.race_chunks);
+    *s_c = __hip_atomic_fetch_add(claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (!__shfl(last, 0)) return;
+  if (!lane_i32(last, 0)) return;
   unsigned long long best = 0ull;
-  for (int32_t c = tid; c < a.race_chunks; c += 64) {
+  for (int32_t c = lane; c < a.race_chunks; c += 64) {
     const unsigned long long v = load_coherent(a.cand + (int64_t)b * a.race_chunks + c);
     best = v > best ? v : best;
   }
@@ -448,40 +489,80 @@ __device__ __forceinline__ void tree_race_block(const TreeArgs<Elem>& a, int32_t
   if (best == 0ull) {  // every token with mass is a child of the stop node: race over p
     float bk = 0.f;
     int32_t bx = INT_MAX;
-    for (int32_t G = tid; G < Gend; G += 64) {
+    for (int32_t G = lane; G < Gend; G += 64) {
       float l[4], qd[4];
       load_group_scalar(lrow, (const float*)nullptr, G, a.V, l, qd);
-      race_group(l, qd, kModeBonus, -1, rec.c, rec.shift, rec.inv_sum, -INFINITY, k0, k1, (uint32_t)rec.n,
-                 (uint32_t)b, G, bk, bx);
+      race_group(l, qd, kModeBonus, -1, cs, shift, inv_sum, -INFINITY, k0, k1, (uint32_t)d, (uint32_t)b, G, bk, bx);
     }
     best = wave_max(pack_key(bk, bx));
   }
-  if (tid == 0) {
-    a.out[(int64_t)b * (a.max_depth + 1) + rec.n] = unpack_token(best);
-    a.nacc[b] = rec.n;
+  if (lane == 0) {
+    a.out[(int64_t)b * (a.max_depth + 1) + d] = unpack_token(best);
+    a.nacc[b] = d;
   }
+  tree_finish(a, b, d, cur);
 }
 
+// Workgroup k of request b = blockIdx / K: works through the request's
+// entries in order, claiming chunks of each until none is left.
 template <typename Elem, int NV>
 __global__ __launch_bounds__(kRowThreads) void tree_walk_kernel(TreeArgs<Elem> a) {
-  __shared__ unsigned long long s_w;
-  int64_t k = blockIdx.x;
-  const int64_t layer0 = (int64_t)a.B * a.nsplit;                 // root rows
-  const int64_t per_layer = (int64_t)a.B * kTreeSlots * a.nsplit;  // layers 1 .. max_depth
-  if (k < layer0) {
-    tree_walk_block<Elem, NV>(a, 0, (int32_t)(k / a.nsplit), 0, (int32_t)(k % a.nsplit), &s_w);
-    return;
+  __shared__ unsigned long long s_e, s_w;
+  __shared__ uint32_t s_c;
+  const int32_t b = (int32_t)(blockIdx.x / a.K);
+  const int tid = threadIdx.x, lane = tid & 63;
+  // The request's nodes once for all its entries (lane i = node i, wavefront
+  // 0, for the decisions); loaded only if the range is in bounds (the init
+  // kernel validated the rest; an invalid request gets no row entry).
+  const int32_t s = a.cu[b], e = a.cu[b + 1];
+  const int32_t n = e - s;
+  const float T = a.temperature[b];
+  int32_t tok = 0, par = -2;
+  if (tid < 64 && s >= 0 && s <= e && e <= a.N && n <= kTreeMaxNodes && lane < n) {
+    tok = a.tokens[s + lane];
+    par = a.parents[s + lane];
   }
-  k -= layer0;
-  if (k < per_layer * a.max_depth) {
-    const int32_t d = 1 + (int32_t)(k / per_layer);
-    const int64_t r = k % per_layer;  // request, then slot, then chunk
-    tree_walk_block<Elem, NV>(a, d, (int32_t)(r / ((int64_t)kTreeSlots * a.nsplit)),
-                              (int32_t)((r / a.nsplit) % kTreeSlots), (int32_t)(r % a.nsplit), &s_w);
-    return;
+  const unsigned long long* E = entries_of(a, b);
+  uint32_t* C = claims_of(a, b);
+  for (int32_t r = 0; r < kTreeEntries; ++r) {
+    if (tid == 0) {
+      // a chunk of entry r is claimed at once; the entry and the walk word are polled together
+      s_c = __hip_atomic_fetch_add(C + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      unsigned long long ent = load_coherent(E + r), w = load_coherent(walk_of(a, b));
+      for (int32_t i = 0; !ent && i < kTreePollLimit; ++i) {
+        __builtin_amdgcn_s_sleep(4);
+        ent = load_coherent(E + r);
+        w = load_coherent(walk_of(a, b));
+      }
+      s_e = ent;
+      s_w = w;
+    }
+    __syncthreads();
+    const unsigned long long ent = s_e, w = s_w;
+    uint32_t c = s_c;
+    __syncthreads();  // s_e, s_w and s_c are rewritten below
+    if (!ent || entry_kind(ent) == kEntryExit) return;
+    const uint32_t chunks = (uint32_t)entry_chunks(ent);
+    const int32_t x = entry_node(ent), d = entry_step(ent);
+    const bool race = entry_kind(ent) == kEntryRace;
+    bool merged = false;  // a race entry's row statistics, once per workgroup
+    float shift = 0.f, inv_sum = 0.f;
+    // a row the walk can no longer need: it stopped, passed step d, or reached another node at it
+    const uint32_t step = walk_step(w);
+    if (!race && (walk_status(w) != kWalking || step > (uint32_t)d || (step == (uint32_t)d && walk_node(w) != x)))
+      continue;
+    while (c < chunks) {
+      // thread 0 claims the next chunk as the finished one is counted (the two
+      // atomics travel together), into s_c
+      if (race)
+        tree_race_chunk<Elem>(a, b, d, x, (int32_t)c, s, n, T, tok, par, merged, shift, inv_sum, C + r, &s_c);
+      else
+        tree_row_chunk<Elem, NV>(a, b, d, x, (int32_t)c, s, n, T, tok, par, C + r, &s_c);
+      __syncthreads();
+      c = s_c;
+      __syncthreads();
+    }
   }
-  k -= per_layer * a.max_depth;
-  tree_race_block<Elem>(a, (int32_t)(k / a.race_chunks), (int32_t)(k % a.race_chunks), &s_w);
 }
 
 }  // namespace rsv

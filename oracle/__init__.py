@@ -68,7 +68,7 @@ def _load():
     lib.rso_verify_filtered.restype = ctypes.c_int
     lib.rso_filtered_probs_row.argtypes = [P, i32, f64, i32, f64, f64, P, P, P]
     lib.rso_filtered_probs_row.restype = None
-    lib.rso_verify_tree.argtypes = [P, i32, P, P, P, P, i32, i32, i32, i32, i32, u64, f64, P, P, P, P, P, i32]
+    lib.rso_verify_tree.argtypes = [P, i32, P, P, P, P, P, i32, i32, i32, i32, i32, u64, f64, P, P, P, P, P, i32]
     lib.rso_verify_tree.restype = ctypes.c_int
     lib.rso_probs.argtypes = [P, i32, P, P, i32, i32, P]
     lib.rso_probs.restype = ctypes.c_int
@@ -178,12 +178,15 @@ class TreeResult:
 
 
 def verify_tree(logits, node_tokens, node_parents, cu_num_nodes, temperature, seed: int, max_nodes: int,
-                max_depth: int, *, eps: float = DEFAULT_EPS, threads: int = 0) -> TreeResult:
+                max_depth: int, *, draft_probs=None, eps: float = DEFAULT_EPS, threads: int = 0) -> TreeResult:
     """Tree verify (rs_oracle.c, rso_verify_tree): request b's rows start at
-    cu[b] + b (row 0 the root position, row 1 + i node i)."""
+    cu[b] + b (row 0 the root position, row 1 + i node i).  draft_probs
+    (optional, fp32, one row per tree position like the logits): the extra
+    token after a stop at node c comes from max(0, p - q_c)."""
     lib = _load()
     lg, code = _logits_arg(logits)
     V = int(lg.shape[-1])
+    q = None if draft_probs is None else _to_numpy(draft_probs, np.float32)
     tok = _to_numpy(node_tokens, np.int32)
     par = _to_numpy(node_parents, np.int32)
     cu = _to_numpy(cu_num_nodes, np.int32)
@@ -192,12 +195,15 @@ def verify_tree(logits, node_tokens, node_parents, cu_num_nodes, temperature, se
     N = int(tok.shape[0])
     if lg.size != (N + B) * V:
         raise ValueError("logits must hold N + B rows")
+    if q is not None and q.size != (N + B) * V:
+        raise ValueError("draft_probs must hold N + B rows")
     out = np.empty((B, max_depth + 1), np.int32)
     path = np.empty((B, max(max_depth, 0)), np.int32)
     nacc = np.empty(B, np.int32)
     flags = np.empty(B, np.int32)
     cand = np.empty((B, NCAND), np.int32)
-    rc = lib.rso_verify_tree(_ptr(lg), code, _ptr(tok), _ptr(par), _ptr(cu), _ptr(T), B, N, int(max_nodes),
+    rc = lib.rso_verify_tree(_ptr(lg), code, None if q is None else _ptr(q), _ptr(tok), _ptr(par), _ptr(cu),
+                             _ptr(T), B, N, int(max_nodes),
                              int(max_depth), V, int(seed) & ((1 << 64) - 1), float(eps), _ptr(out), _ptr(path),
                              _ptr(nacc), _ptr(flags), _ptr(cand), int(threads))
     if rc != 0:

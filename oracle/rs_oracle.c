@@ -565,16 +565,25 @@ int rso_verify(const void* logits, int32_t dtype, const float* q, const int32_t*
  * probability p(its token) and the residual is p without the siblings, so the
  * emitted token at every depth is distributed as p.  A one-child-per-node tree
  * is the chain with one-hot q, with the same random numbers.
+ * With draft distributions q (one row per tree position, aligned with the
+ * target rows: row 0 the prefix position, row 1 + i node i), the extra token
+ * after a stop at node c is the race over max(0, p - q_c) instead, q_c the
+ * row of c [§7.2: after a rejection the extra token is sampled from
+ * relu(target_probs - draft_probs)]; the acceptance roulette is unchanged.
+ * This is the page's rule as written: it keeps p only when q_c is p on the
+ * siblings and 0 elsewhere (then it is the rule above, the same tokens), not
+ * for an arbitrary q (§7.4 calls the target-only path inexact).  An all-zero
+ * residual falls back to the race over p, flagged, as in the chain.
  *   tree tokens [N], parents [N] (request-local node index or -1), cu [B+1];
  *   out [B, max_depth + 1] tokens (-1 padded), path [B, max_depth] node
  *   indices (-1 padded), num_accepted [B]; flags as rso_verify (invalid:
  *   parent >= node or < -1, token outside [0, V), depth beyond max_depth,
  *   more than max_nodes nodes).
  * Returns 0, or -1 on an argument error. */
-int rso_verify_tree(const void* logits, int32_t dtype, const int32_t* tokens, const int32_t* parents,
-                    const int32_t* cu, const float* T, int32_t B, int32_t N, int32_t max_nodes, int32_t max_depth,
-                    int32_t V, uint64_t seed, double eps, int32_t* out, int32_t* path, int32_t* num_accepted,
-                    int32_t* flags, int32_t* cand, int32_t nthreads) {
+int rso_verify_tree(const void* logits, int32_t dtype, const float* q, const int32_t* tokens,
+                    const int32_t* parents, const int32_t* cu, const float* T, int32_t B, int32_t N, int32_t max_nodes,
+                    int32_t max_depth, int32_t V, uint64_t seed, double eps, int32_t* out, int32_t* path,
+                    int32_t* num_accepted, int32_t* flags, int32_t* cand, int32_t nthreads) {
   if (!logits || !cu || !T || !out || !path || !num_accepted || !flags) return -1;
   if (B < 0 || N < 0 || V < 1 || max_nodes < 0 || max_depth < 0 || (N > 0 && (!tokens || !parents))) return -1;
 #ifdef _OPENMP
@@ -647,7 +656,17 @@ int rso_verify_tree(const void* logits, int32_t dtype, const int32_t* tokens, co
             if (fabs(u - cum) <= eps * cum) flags[b] |= RSO_FLAG_ACCEPT_TIE;
             if (u < cum) next = i;
           }
-          if (next < 0) {
+          if (next < 0 && q) {
+            /* residual: max(0, p - q) with the stop node's draft row */
+            const float* qc = q + (row0 + 1 + cur) * (int64_t)V;
+            for (int32_t x = 0; x < V; ++x) {
+              double qx = (double)qc[x];
+              r[x] = fmax(0.0, p[x] - qx);
+              rlo[x] = fmax(0.0, p[x] * (1.0 - eps) - qx);
+              rhi[x] = fmax(0.0, p[x] * (1.0 + eps) - qx);
+            }
+            token = sample_with_fallback(r, rlo, rhi, p, V, seed, b, d, eps, E, &flags[b], cb);
+          } else if (next < 0) {
             /* residual: p without the children's tokens (a childless node: p) */
             for (int32_t x = 0; x < V; ++x) r[x] = p[x];
             for (int32_t i = 0; i < n; ++i)

@@ -16,9 +16,9 @@ int rso_verify(const void*, int32_t, const float*, const int32_t*, const int32_t
 int rso_verify_filtered(const void*, int32_t, const float*, const int32_t*, const int32_t*, const float*,
                         const int32_t*, const float*, int32_t, int32_t, int32_t, int32_t, uint64_t, int32_t, double,
                         int32_t*, int32_t*, int32_t*, double*, int32_t*, int32_t);
-int rso_verify_tree(const void*, int32_t, const int32_t*, const int32_t*, const int32_t*, const float*, int32_t,
-                    int32_t, int32_t, int32_t, int32_t, uint64_t, double, int32_t*, int32_t*, int32_t*, int32_t*,
-                    int32_t*, int32_t);
+int rso_verify_tree(const void*, int32_t, const float*, const int32_t*, const int32_t*, const int32_t*,
+                    const float*, int32_t, int32_t, int32_t, int32_t, int32_t, uint64_t, double, int32_t*, int32_t*,
+                    int32_t*, int32_t*, int32_t*, int32_t);
 int rso_probs(const void*, int32_t, const int32_t*, const float*, int32_t, int32_t, double*);
 void rso_filtered_probs_row(const double*, int32_t, double, int32_t, double, double, double*, double*, int*);
 
@@ -138,11 +138,18 @@ static void tree_case(int32_t V, int dtype) {
   for (int64_t i = 0; i < (int64_t)R * V; ++i) lb[i] = to_bf16(lf[i] = (float)(2.0 * gauss()));
   float T[5] = {1.0f, 0.0f, 0.7f, 1.2f, -1.0f};
   int32_t out[5 * 5], path[5 * 4], nacc[5], flags[5], cand[5 * 8];
-  CHECK(rso_verify_tree(dtype ? (const void*)lb : (const void*)lf, dtype, tok, parents, cu, T, B, B * n, n,
+  CHECK(rso_verify_tree(dtype ? (const void*)lb : (const void*)lf, dtype, NULL, tok, parents, cu, T, B, B * n, n,
                         max_depth, V, 3, 1e-6, out, path, nacc, flags, cand, 2) == 0);
   CHECK(nacc[3] == -1);
   for (int32_t b = 0; b < B; ++b)
     if (b != 3) CHECK(nacc[b] >= 0 && nacc[b] <= max_depth);
+  /* with draft distributions: one row per tree position */
+  float* q = malloc(sizeof(float) * (size_t)R * V);
+  for (int64_t i = 0; i < (int64_t)R * V; ++i) q[i] = (float)(unif() * 2.0 / V);
+  CHECK(rso_verify_tree(dtype ? (const void*)lb : (const void*)lf, dtype, q, tok, parents, cu, T, B, B * n, n,
+                        max_depth, V, 3, 1e-6, out, path, nacc, flags, cand, 2) == 0);
+  CHECK(nacc[3] == -1);
+  free(q);
   free(lf);
   free(lb);
 }

@@ -67,9 +67,10 @@ def _chi2(counts, probs):
     exp = np.asarray(probs, np.float64) * counts.sum()
     assert counts[exp == 0].sum() == 0
     keep = exp >= 5
+    small = (exp > 0) & ~keep  # lumped into one bin; impossible outcomes (checked empty above) are left out
     obs, ex = counts[keep], exp[keep]
-    if (~keep).any():
-        obs, ex = np.append(obs, counts[~keep].sum()), np.append(ex, exp[~keep].sum())
+    if small.any():
+        obs, ex = np.append(obs, counts[small].sum()), np.append(ex, exp[small].sum())
     return stats.chisquare(obs, ex * obs.sum() / ex.sum()).pvalue
 
 
@@ -164,3 +165,90 @@ def test_every_token_drafted_never_reaches_the_zero_residual():
                            np.full(B, 0.9, np.float32), 3, n, 3)
     assert (r.num_accepted >= 1).all()
     assert not (r.flags & oracle.FLAG_ZERO_RESIDUAL).any()
+
+
+# ---- draft distributions: the extra token after a stop from max(0, p - q) ----
+# [投机解码（Speculative Decoding）端到端深挖 §7.2: after a rejection the extra
+# token is sampled from relu(target_probs - draft_probs)]
+
+def _probs_rows(w):
+    return oracle.probs(w.logits, w.cu_num_nodes, w.temperature)
+
+
+def test_q_on_the_siblings_is_the_default_rule():
+    """q_c = p_c on the tokens of c's children and 0 elsewhere makes
+    max(0, p - q) the residual p without the siblings: the same tokens as
+    without draft distributions, request for request."""
+    import torch
+    w = W.make_tree(24, 300, depth=4, branching=(3, 2, 2, 1), max_nodes=40, dtype=torch.float32,
+                    temperature=("uniform", 0.5, 1.2), draft_noise=0.7, seed=5, gen_seed=15)
+    p = _probs_rows(w)
+    tok, par = w.node_tokens.numpy(), w.node_parents.numpy()
+    cu = w.cu_num_nodes.numpy()
+    q = np.zeros_like(p, dtype=np.float32)
+    for b in range(w.B):
+        s, e = int(cu[b]), int(cu[b + 1])
+        for c in range(-1, e - s):
+            row = s + b + 1 + c
+            kids = tok[s:e][par[s:e] == c]
+            q[row, kids] = p[row, kids]
+    a = oracle.verify_tree(w.logits, w.node_tokens, w.node_parents, w.cu_num_nodes, w.temperature, w.seed,
+                           w.max_nodes, w.max_depth)
+    g = oracle.verify_tree(w.logits, w.node_tokens, w.node_parents, w.cu_num_nodes, w.temperature, w.seed,
+                           w.max_nodes, w.max_depth, draft_probs=q)
+    ok = ~(a.near_tie | g.near_tie)
+    assert ok.sum() >= w.B - 2
+    np.testing.assert_array_equal(g.num_accepted[ok], a.num_accepted[ok])
+    np.testing.assert_array_equal(g.tokens[ok], a.tokens[ok])
+    np.testing.assert_array_equal(g.path[ok], a.path[ok])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("qkind", ["dirichlet", "peaked"])
+def test_q_one_layer_law(qkind):
+    """One layer of siblings S under the root: sibling s is accepted with
+    probability p(s) (the roulette ignores q), and a stop emits max(0, p - q) /
+    Z, so the first token's law is p(x) [x in S] + (1 - p(S)) max(0, p - q)(x) / Z."""
+    V, B, T = 8, 400_000, 0.9
+    rng = np.random.default_rng(21 if qkind == "dirichlet" else 22)
+    sib = [2, 5]
+    L = (rng.standard_normal((1 + len(sib), V)) * 1.2).astype(np.float32)
+    p = special.softmax(L[0].astype(np.float64) / np.float32(T))
+    q0 = rng.dirichlet(np.ones(V)) if qkind == "dirichlet" else np.eye(V)[np.argmax(p)] * 0.9 + 0.1 / V
+    Q = np.tile(rng.dirichlet(np.ones(V), size=1 + len(sib)).astype(np.float32), (1, 1))
+    Q[0] = q0.astype(np.float32)
+    m = len(sib)
+    lg = np.ascontiguousarray(np.broadcast_to(L, (B, 1 + m, V)).reshape(B * (1 + m), V))
+    qq = np.ascontiguousarray(np.broadcast_to(Q, (B, 1 + m, V)).reshape(B * (1 + m), V))
+    tokens = np.tile(np.array(sib, np.int32), B)
+    parents = np.full(B * m, -1, np.int32)
+    cu = (np.arange(B + 1) * m).astype(np.int32)
+    r = oracle.verify_tree(lg, tokens, parents, cu, np.full(B, T, np.float32), 99, m, 2, draft_probs=qq)
+    assert r.near_tie.mean() < 1e-4
+    res = np.maximum(0.0, p - Q[0].astype(np.float64))
+    pS = sum(p[s] for s in sib)
+    law = (1 - pS) * res / res.sum()
+    for s in sib:
+        law[s] += p[s]
+    assert _chi2(np.bincount(r.tokens[:, 0], minlength=V), law) > PVAL
+
+
+def test_q_all_zero_residual_falls_back_to_p():
+    """q = 2p at the root: max(0, p - q) is zero everywhere, so every stop at
+    the root takes the race over p, flagged (as in the chain)."""
+    V, B, T = 8, 4000, 1.0
+    rng = np.random.default_rng(8)
+    L = (rng.standard_normal((2, V)) * 1.0).astype(np.float32)
+    p = special.softmax(L[0].astype(np.float64) / np.float32(T))
+    Q = np.stack([2 * p, np.full(V, 1.0 / V)]).astype(np.float32)
+    lg = np.ascontiguousarray(np.broadcast_to(L, (B, 2, V)).reshape(B * 2, V))
+    qq = np.ascontiguousarray(np.broadcast_to(Q, (B, 2, V)).reshape(B * 2, V))
+    tokens = np.full(B, int(np.argmin(p)), np.int32)  # an unlikely child: most requests stop at the root
+    cu = np.arange(B + 1, dtype=np.int32)
+    r = oracle.verify_tree(lg, tokens, np.full(B, -1, np.int32), cu, np.full(B, T, np.float32), 5, 1, 2,
+                           draft_probs=qq)
+    stop = r.num_accepted == 0
+    assert stop.mean() > 0.8
+    assert ((r.flags[stop] & oracle.FLAG_ZERO_RESIDUAL) != 0).all()
+    assert not (r.flags[~stop] & oracle.FLAG_ZERO_RESIDUAL).any()
+    assert _chi2(np.bincount(r.tokens[stop, 0], minlength=V), p) > PVAL

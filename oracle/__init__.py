@@ -182,7 +182,8 @@ def verify_tree(logits, node_tokens, node_parents, cu_num_nodes, temperature, se
     """Tree verify (rs_oracle.c, rso_verify_tree): request b's rows start at
     cu[b] + b (row 0 the root position, row 1 + i node i).  draft_probs
     (optional, fp32, one row per tree position like the logits): the extra
-    token after a stop at node c comes from max(0, p - q_c)."""
+    token after a stop at node c comes from max(0, p - q_c) when c has
+    children (a childless node's extra token follows p)."""
     lib = _load()
     lg, code = _logits_arg(logits)
     V = int(lg.shape[-1])

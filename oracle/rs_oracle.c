@@ -573,7 +573,9 @@ int rso_verify(const void* logits, int32_t dtype, const float* q, const int32_t*
  * This is the page's rule as written: it keeps p only when q_c is p on the
  * siblings and 0 elsewhere (then it is the rule above, the same tokens), not
  * for an arbitrary q (§7.4 calls the target-only path inexact).  An all-zero
- * residual falls back to the race over p, flagged, as in the chain.
+ * residual falls back to the race over p, flagged, as in the chain.  A stop
+ * at a childless node rejected nothing, so its extra token is the race over p
+ * whatever q_c holds (the bonus after a full acceptance).
  *   tree tokens [N], parents [N] (request-local node index or -1), cu [B+1];
  *   out [B, max_depth + 1] tokens (-1 padded), path [B, max_depth] node
  *   indices (-1 padded), num_accepted [B]; flags as rso_verify (invalid:
@@ -646,8 +648,10 @@ int rso_verify_tree(const void* logits, int32_t dtype, const float* q, const int
         } else {
           rso_softmax_row(l, V, Tb, p);
           double u = rso_accept_uniform(seed, b, d), cum = 0.0;
+          int32_t kids = 0;
           for (int32_t i = 0; i < n && next < 0; ++i) {
             if (parents[s + i] != cur) continue;
+            ++kids;
             int dup = 0;
             for (int32_t k = 0; k < i; ++k)
               if (parents[s + k] == cur && tokens[s + k] == tokens[s + i]) dup = 1;
@@ -656,8 +660,11 @@ int rso_verify_tree(const void* logits, int32_t dtype, const float* q, const int
             if (fabs(u - cum) <= eps * cum) flags[b] |= RSO_FLAG_ACCEPT_TIE;
             if (u < cum) next = i;
           }
-          if (next < 0 && q) {
-            /* residual: max(0, p - q) with the stop node's draft row */
+          if (next < 0 && q && kids > 0) {
+            /* residual after the siblings were turned down: max(0, p - q) with
+             * the stop node's draft row.  A childless node proposed nothing,
+             * so nothing was rejected there and its extra token follows p
+             * (the branch below, with no tokens to take out). */
             const float* qc = q + (row0 + 1 + cur) * (int64_t)V;
             for (int32_t x = 0; x < V; ++x) {
               double qx = (double)qc[x];

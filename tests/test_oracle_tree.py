@@ -252,3 +252,24 @@ def test_q_all_zero_residual_falls_back_to_p():
     assert ((r.flags[stop] & oracle.FLAG_ZERO_RESIDUAL) != 0).all()
     assert not (r.flags[~stop] & oracle.FLAG_ZERO_RESIDUAL).any()
     assert _chi2(np.bincount(r.tokens[stop, 0], minlength=V), p) > PVAL
+
+
+def test_q_ignored_at_a_childless_node():
+    """A walk that ends at a leaf rejected nothing: the extra token follows the
+    leaf's p whatever its draft row holds (here q peaked on p's mode, which
+    max(0, p - q) would never emit)."""
+    V, B, T = 6, 20000, 1.0
+    rng = np.random.default_rng(12)
+    L = (rng.standard_normal((2, V)) * 1.0).astype(np.float32)
+    L[0, 3] += 6.0  # the root almost always accepts its one child, token 3
+    p_leaf = special.softmax(L[1].astype(np.float64) / np.float32(T))
+    Q = np.stack([np.full(V, 1.0 / V), np.eye(V)[np.argmax(p_leaf)]]).astype(np.float32)
+    lg = np.ascontiguousarray(np.broadcast_to(L, (B, 2, V)).reshape(B * 2, V))
+    qq = np.ascontiguousarray(np.broadcast_to(Q, (B, 2, V)).reshape(B * 2, V))
+    cu = np.arange(B + 1, dtype=np.int32)
+    r = oracle.verify_tree(lg, np.full(B, 3, np.int32), np.full(B, -1, np.int32), cu, np.full(B, T, np.float32), 6,
+                           1, 2, draft_probs=qq)
+    leaf = r.num_accepted == 1
+    assert leaf.mean() > 0.9
+    assert _chi2(np.bincount(r.tokens[leaf, 1], minlength=V), p_leaf) > PVAL
+    assert (r.tokens[leaf, 1] == np.argmax(p_leaf)).mean() > 0.5 * p_leaf.max()

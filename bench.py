@@ -481,39 +481,41 @@ def main():
             f"tau {variants['accept_stats']['accept_length']:.4f}")
 
         # tree verify (rs_verify_tree): B=64 EAGLE-style draft trees of 60 nodes
-        # (branching 4, 2, 2, 1, 1; depth 5) at the same V, T ~ U[0.5, 1.2]
-        trees = [W.make_tree(64, w0.V, temperature=("uniform", 0.5, 1.2), seed=7, gen_seed=5000 + i, device=dev)
-                 for i in range(args.copies)]
-        tw = trees[0]
-        tws = torch.empty((rs.load_library().rs_verify_tree_workspace_size(tw.B, tw.V),), dtype=torch.uint8,
-                          device=dev)
-        tout = torch.empty((tw.B, tw.max_depth + 1), dtype=torch.int32, device=dev)
-        tpath = torch.empty((tw.B, tw.max_depth), dtype=torch.int32, device=dev)
-        tn = torch.empty((tw.B,), dtype=torch.int32, device=dev)
+        # (branching 4, 2, 2, 1, 1; depth 5) at the same V, T ~ U[0.5, 1.2];
+        # then the same with the draft distributions (fp32, every tree position)
+        for with_q, key in ((False, "tree_eagle_B64"), (True, "tree_eagle_B64_draft_probs")):
+            trees = [W.make_tree(64, w0.V, temperature=("uniform", 0.5, 1.2), seed=7, gen_seed=5000 + i, device=dev,
+                                 with_q=with_q) for i in range(args.copies)]
+            tw = trees[0]
+            tws = torch.empty((rs.load_library().rs_verify_tree_workspace_size(tw.B, tw.V),), dtype=torch.uint8,
+                              device=dev)
+            tout = torch.empty((tw.B, tw.max_depth + 1), dtype=torch.int32, device=dev)
+            tpath = torch.empty((tw.B, tw.max_depth), dtype=torch.int32, device=dev)
+            tn = torch.empty((tw.B,), dtype=torch.int32, device=dev)
 
-        def tree_call(k):
-            t = trees[k % args.copies]
-            rs.verify_tree(t.logits, t.node_tokens, t.node_parents, t.cu_num_nodes, t.temperature, seed=t.seed,
-                           max_nodes=t.max_nodes, max_depth=t.max_depth, out=tout, accepted_nodes=tpath,
-                           num_accepted=tn, workspace=tws, stream=stream)
+            def tree_call(k):
+                t = trees[k % args.copies]
+                rs.verify_tree(t.logits, t.node_tokens, t.node_parents, t.cu_num_nodes, t.temperature, seed=t.seed,
+                               max_nodes=t.max_nodes, max_depth=t.max_depth, draft_probs=t.draft_probs, out=tout,
+                               accepted_nodes=tpath, num_accepted=tn, workspace=tws, stream=stream)
 
-        st = timed_region(tree_call, args.steps, args.warmup, stream)
-        rows_read = []
-        for i in range(args.copies):
-            tree_call(i)
-            torch.cuda.synchronize()
-            rows_read.append(int((tn.cpu().numpy() + 1).sum()))
-        tsec = st["ms_per_step"] / 1e3
-        dense = (tw.N + tw.B) * tw.V * tw.logits.element_size()
-        needed_t = float(np.mean(rows_read)) * tw.V * tw.logits.element_size()
-        variants["tree_eagle_B64"] = {
-            **st, "nodes_per_s": tw.N / tsec, "nodes": tw.N, "rows": tw.N + tw.B,
-            "rows_streamed": float(np.mean(rows_read)), "needed_frac": needed_t / tsec / 1e9 / HBM_PEAK_GBPS,
-            "every_row_GBps": dense / tsec / 1e9}
-        log(f"tree (B=64, {tw.max_nodes} nodes, depth {tw.max_depth}): {st['ms_per_step'] * 1e3:.1f} us/step "
-            f"(median {st['median_ms'] * 1e3:.1f}), {tw.N / tsec:.3g} nodes/s, {np.mean(rows_read):.0f} of "
-            f"{tw.N + tw.B} rows streamed")
-        del trees
+            st = timed_region(tree_call, args.steps, args.warmup, stream)
+            rows_read = []
+            for i in range(args.copies):
+                tree_call(i)
+                torch.cuda.synchronize()
+                rows_read.append(int((tn.cpu().numpy() + 1).sum()))
+            tsec = st["ms_per_step"] / 1e3
+            dense = (tw.N + tw.B) * tw.V * tw.logits.element_size()
+            needed_t = float(np.mean(rows_read)) * tw.V * tw.logits.element_size()
+            variants[key] = {
+                **st, "nodes_per_s": tw.N / tsec, "nodes": tw.N, "rows": tw.N + tw.B,
+                "rows_streamed": float(np.mean(rows_read)), "needed_frac": needed_t / tsec / 1e9 / HBM_PEAK_GBPS,
+                "every_row_GBps": dense / tsec / 1e9}
+            log(f"{key} (B=64, {tw.max_nodes} nodes, depth {tw.max_depth}): {st['ms_per_step'] * 1e3:.1f} us/step "
+                f"(median {st['median_ms'] * 1e3:.1f}), {tw.N / tsec:.3g} nodes/s, {np.mean(rows_read):.0f} of "
+                f"{tw.N + tw.B} rows streamed")
+            del trees, tree_call
 
         # n-gram proposer (rs_ngram_propose): B=64 contexts of 4096 tokens,
         # min_n 3, max_n 8, k 5 (the pages' example settings)

@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define RS_VERIFY_ABI_VERSION 1
+#define RS_VERIFY_ABI_VERSION 2
 #define RS_MAX_SPEC_LEN 32 /* [第12章 §12.5.4: MAX_SPEC_LEN = 32] */
 
 /* Both enums span every 32-bit value (the *_ENUM_MAX sentinels), so any int a
@@ -262,12 +262,26 @@ rs_status rs_verify_greedy(const void* target_logits, rs_dtype logits_dtype,
  * Every sibling is accepted with probability p(its token) and the residual is
  * p without the siblings, so each emitted token follows p; a tree with one
  * child per node is exactly the chain of rs_verify with draft_probs = NULL
- * (same tokens for the same seed).  Trees carry no draft probabilities.
+ * (same tokens for the same seed).
+ * With draft_probs (one draft distribution per tree position), the extra token
+ * after a stop at node c is the race over max(0, p - q_c) instead, q_c the
+ * stop node's row [§7.2: after a rejection, from relu(target_probs -
+ * draft_probs)]; acceptance is the same roulette.  This is the page's rule
+ * as written: it leaves each emitted token distributed as p when q_c is p on
+ * c's children and 0 elsewhere (then it equals the rule above), not for an
+ * arbitrary q (§7.4).  An all-zero residual falls back to the race over p.
+ * A stop at a childless node rejected nothing: its extra token is the race
+ * over p whatever its draft row holds.  A draft_probs pointer that is not
+ * 16-byte aligned gives RS_ERR_UNSUPPORTED.
  * Layout:
  *   cu_num_nodes  [B+1] int32: request b owns nodes cu[b] .. cu[b+1]-1
  *   target_logits [N + B, V] fp32 / bf16: request b's rows start at
  *                 cu[b] + b; row 0 is the prefix position (it predicts the
  *                 children of the root), row 1 + i is node i
+ *   draft_probs   [N + B, V] fp32 or NULL: rows aligned with target_logits
+ *                 (row 0 of a request the draft distribution at the prefix
+ *                 position, row 1 + i at node i), non-negative; a row
+ *                 need not sum to 1; 16-byte aligned
  *   node_tokens   [N] int32 in [0, V); node_parents [N] int32, request-local,
  *                 -1 <= parent < node
  *   temperature   [B] fp32
@@ -289,8 +303,9 @@ rs_status rs_verify_greedy(const void* target_logits, rs_dtype logits_dtype,
  * Ownership, asynchrony and error reporting as for rs_verify. */
 #define RS_MAX_TREE_NODES 64
 size_t rs_verify_tree_workspace_size(int32_t batch, int32_t vocab);
-rs_status rs_verify_tree(const void* target_logits, rs_dtype logits_dtype, const int32_t* node_tokens,
-                         const int32_t* node_parents, const int32_t* cu_num_nodes, const float* temperature,
+rs_status rs_verify_tree(const void* target_logits, rs_dtype logits_dtype, const float* draft_probs,
+                         const int32_t* node_tokens, const int32_t* node_parents, const int32_t* cu_num_nodes,
+                         const float* temperature,
                          int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_depth,
                          int32_t vocab, uint64_t seed, int32_t* output_token_ids,
                          int32_t* accepted_nodes, int32_t* num_accepted, void* workspace,

@@ -80,7 +80,7 @@ def load_library(path: str = LIB_PATH):
     lib.rs_verify_filtered.restype = ctypes.c_int
     lib.rs_verify_greedy.argtypes = [P, ctypes.c_int, P, P, i32, i32, i32, i32, P, P, P, sz, P]
     lib.rs_verify_greedy.restype = ctypes.c_int
-    lib.rs_verify_tree.argtypes = [P, ctypes.c_int, P, P, P, P, i32, i32, i32, i32, i32, u64, P, P, P, P, sz, P]
+    lib.rs_verify_tree.argtypes = [P, ctypes.c_int, P, P, P, P, P, i32, i32, i32, i32, i32, u64, P, P, P, P, sz, P]
     lib.rs_verify_tree_workspace_size.argtypes = [i32, i32]
     lib.rs_verify_tree_workspace_size.restype = sz
     lib.rs_verify_tree.restype = ctypes.c_int
@@ -370,11 +370,13 @@ def accept_length(counters) -> float:
 
 def verify_tree(target_logits: torch.Tensor, node_tokens: torch.Tensor, node_parents: torch.Tensor,
                 cu_num_nodes: torch.Tensor, temperature: torch.Tensor, *, seed: int, max_nodes: int, max_depth: int,
-                out: Optional[torch.Tensor] = None, accepted_nodes: Optional[torch.Tensor] = None,
-                num_accepted: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                stream: Optional[torch.cuda.Stream] = None):
-    """Tree verify (rs_verify_tree).  Returns (output_token_ids [B, max_depth+1],
-    accepted_nodes [B, max_depth], num_accepted [B])."""
+                draft_probs: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                accepted_nodes: Optional[torch.Tensor] = None, num_accepted: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None):
+    """Tree verify (rs_verify_tree).  draft_probs (optional, fp32, one row per
+    tree position like target_logits): the extra token after a stop comes from
+    max(0, p - q) of the stop node's row.  Returns (output_token_ids
+    [B, max_depth+1], accepted_nodes [B, max_depth], num_accepted [B])."""
     lib = load_library()
     if not isinstance(target_logits, torch.Tensor) or target_logits.device.type != "cuda":
         raise ValueError("target_logits must be a CUDA (HIP) tensor")
@@ -392,6 +394,10 @@ def verify_tree(target_logits: torch.Tensor, node_tokens: torch.Tensor, node_par
         raise ValueError("node_parents needs N entries, temperature B, cu_num_nodes B + 1")
     if target_logits.numel() != (N + B) * V:
         raise ValueError(f"target_logits must hold N + B = {N + B} rows")
+    if draft_probs is not None:
+        _dev_tensor(draft_probs, "draft_probs", torch.float32, dev)
+        if draft_probs.numel() != (N + B) * V:
+            raise ValueError(f"draft_probs must hold N + B = {N + B} rows of V")
     if out is None:
         out = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
     if accepted_nodes is None:
@@ -410,7 +416,8 @@ def verify_tree(target_logits: torch.Tensor, node_tokens: torch.Tensor, node_par
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     _check(lib.rs_verify_tree(
-        target_logits.data_ptr(), _DTYPE[target_logits.dtype], node_tokens.data_ptr() if N > 0 else None,
+        target_logits.data_ptr(), _DTYPE[target_logits.dtype],
+        draft_probs.data_ptr() if draft_probs is not None else None, node_tokens.data_ptr() if N > 0 else None,
         node_parents.data_ptr() if N > 0 else None, cu_num_nodes.data_ptr(), temperature.data_ptr(), B, N,
         int(max_nodes), int(max_depth), V, int(seed) & ((1 << 64) - 1), out.data_ptr(),
         accepted_nodes.data_ptr() if max_depth > 0 else None, num_accepted.data_ptr(), workspace.data_ptr(),

@@ -708,14 +708,15 @@ static int64_t tree_resident() {
 }
 
 template <typename Elem>
-static rs_status launch_tree(const void* logits, const int32_t* node_tokens, const int32_t* node_parents,
-                             const int32_t* cu, const float* temperature, int32_t B, int32_t N, int32_t max_nodes,
+static rs_status launch_tree(const void* logits, const float* q, const int32_t* node_tokens,
+                             const int32_t* node_parents, const int32_t* cu, const float* temperature, int32_t B, int32_t N, int32_t max_nodes,
                              int32_t max_depth, int32_t V, uint64_t seed, int32_t* out, int32_t* path,
                              int32_t* nacc, void* ws, hipStream_t stream) {
   const TreeLayout t = tree_layout(B, V);
   char* w = static_cast<char*>(ws);
   TreeArgs<Elem> a;
   a.logits = static_cast<const Elem*>(logits);
+  a.q = q;
   a.tokens = node_tokens;
   a.parents = node_parents;
   a.cu = cu;
@@ -816,8 +817,9 @@ size_t rs_verify_tree_workspace_size(int32_t batch, int32_t vocab) {
   return rsv::tree_layout(batch, vocab).total;
 }
 
-rs_status rs_verify_tree(const void* target_logits, rs_dtype logits_dtype, const int32_t* node_tokens,
-                         const int32_t* node_parents, const int32_t* cu_num_nodes, const float* temperature,
+rs_status rs_verify_tree(const void* target_logits, rs_dtype logits_dtype, const float* draft_probs,
+                         const int32_t* node_tokens, const int32_t* node_parents, const int32_t* cu_num_nodes,
+                         const float* temperature,
                          int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_depth, int32_t vocab,
                          uint64_t seed, int32_t* output_token_ids, int32_t* accepted_nodes, int32_t* num_accepted,
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -833,19 +835,19 @@ rs_status rs_verify_tree(const void* target_logits, rs_dtype logits_dtype, const
   const size_t es = logits_dtype == RS_BF16 ? 2 : 4;
   if (((uintptr_t)target_logits % es) || ((uintptr_t)node_tokens % 4) || ((uintptr_t)node_parents % 4) ||
       ((uintptr_t)cu_num_nodes % 4) || ((uintptr_t)temperature % 4) || ((uintptr_t)output_token_ids % 4) ||
-      ((uintptr_t)accepted_nodes % 4) || ((uintptr_t)num_accepted % 4))
+      ((uintptr_t)accepted_nodes % 4) || ((uintptr_t)num_accepted % 4) || ((uintptr_t)draft_probs % 16))
     return RS_ERR_UNSUPPORTED;
   // entry words hold a row's chunk count in 24 bits; the grid, B * K <= max(B, resident), stays below 2^31
   const rsv::TreeLayout t = rsv::tree_layout(batch, vocab);
   if (t.nsplit_max >= (1 << 24) || t.race_chunks >= (1 << 24)) return RS_ERR_UNSUPPORTED;
   if (!workspace || ((uintptr_t)workspace % 16) || workspace_bytes < t.total) return RS_ERR_WORKSPACE;
   if (logits_dtype == RS_BF16)
-    return rsv::launch_tree<uint16_t>(target_logits, node_tokens, node_parents, cu_num_nodes, temperature, batch,
-                                 total_nodes, max_nodes, max_depth, vocab, seed, output_token_ids, accepted_nodes,
-                                 num_accepted, workspace, stream);
-  return rsv::launch_tree<float>(target_logits, node_tokens, node_parents, cu_num_nodes, temperature, batch, total_nodes,
-                            max_nodes, max_depth, vocab, seed, output_token_ids, accepted_nodes, num_accepted,
-                            workspace, stream);
+    return rsv::launch_tree<uint16_t>(target_logits, draft_probs, node_tokens, node_parents, cu_num_nodes,
+                                      temperature, batch, total_nodes, max_nodes, max_depth, vocab, seed,
+                                      output_token_ids, accepted_nodes, num_accepted, workspace, stream);
+  return rsv::launch_tree<float>(target_logits, draft_probs, node_tokens, node_parents, cu_num_nodes, temperature,
+                                 batch, total_nodes, max_nodes, max_depth, vocab, seed, output_token_ids,
+                                 accepted_nodes, num_accepted, workspace, stream);
 }
 
 rs_status rs_ngram_propose(const int32_t* context_token_ids, const int32_t* cu_context, int32_t batch,

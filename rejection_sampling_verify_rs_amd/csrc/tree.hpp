@@ -29,7 +29,9 @@
 // a list of entries that its workgroups work through in order:
 //   a row entry (node x, step d): stream the row of x (the root: -1) in
 //     chunks of 8 vectors per thread into that row's partial statistics;
-//   a race entry (stop node, step d): race the stop row in 8192-token chunks;
+//   a race entry (stop node, step d): race the stop row in 8192-token chunks
+//     (p without the stop node's children, or max(0, p - q) with the stop
+//     node's draft row q);
 //   an exit entry: the request is finished.
 // A workgroup claims chunks of the entry it is at from that entry's counter
 // (the first claim is made while the entry may still be unwritten), so a row
@@ -137,6 +139,7 @@ __device__ __forceinline__ int32_t nth_bit(unsigned long long m, int32_t i) {
 template <typename Elem>
 struct TreeArgs {
   const Elem* logits;
+  const float* q;  // draft distributions, one row per tree position (NULL: none)
   const int32_t* tokens;
   const int32_t* parents;
   const int32_t* cu;
@@ -406,10 +409,11 @@ __device__ __forceinline__ void tree_row_chunk(const TreeArgs<Elem>& a, int32_t 
 
 // Race chunk rc (kRaceThreads * kTreeRaceTPT tokens) of request b's stop row
 // (node cur, step d), the stop node's children (those with a token in the
-// chunk) marked in an LDS bitmap and given weight 0.  The row's statistics
-// are merged at a workgroup's first chunk of the entry (`merged`) and kept.
-// The last chunk to arrive writes the extra token; if every token with mass
-// was a child of the stop node it races over p instead.
+// chunk) marked in an LDS bitmap and given weight 0 -- or, with draft
+// distributions, every token weighted max(0, p - q) with the stop node's
+// draft row.  The row's statistics are merged at a workgroup's first chunk of
+// the entry (`merged`) and kept.  The last chunk to arrive writes the extra
+// token; if no token had weight it races over p instead.
 template <typename Elem>
 __device__ __forceinline__ void tree_race_chunk(const TreeArgs<Elem>& a, int32_t b, int32_t d, int32_t cur,
                                                 int32_t rc, int32_t s, int32_t n, float T, int32_t tok, int32_t par,
@@ -420,11 +424,22 @@ __device__ __forceinline__ void tree_race_chunk(const TreeArgs<Elem>& a, int32_t
   using R4 = Raw4<Elem>;
   __shared__ uint32_t bits[kChunk / 32];
   __shared__ unsigned long long lds_u[kRaceThreads / 64];
+  __shared__ int s_kids;
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t row = (int64_t)s + b + 1 + cur;
   const float cs = scale_of(T);
   const Elem* lrow = a.logits + row * a.V;
-  const bool fast = ((uintptr_t)lrow % sizeof(typename R4::T)) == 0;
+  bool kids = false;
+  if (a.q) {  // only a node whose children were turned down races max(0, p - q); a childless one races p
+    if (tid < 64) {  // wavefront 0 holds the nodes
+      const bool k = __ballot(lane < n && par == cur) != 0ull;
+      if (lane == 0) s_kids = k;
+    }
+    __syncthreads();
+    kids = s_kids != 0;
+  }
+  const float* qrow = kids ? a.q + row * a.V : nullptr;  // the stop node's draft row
+  const bool fast = ((uintptr_t)lrow % sizeof(typename R4::T)) == 0 && ((uintptr_t)qrow % 16) == 0;
   const int32_t Gend = (a.V + 3) / 4, Gfull = fast ? a.V / 4 : 0;
   const int32_t G0 = rc * (kRaceThreads * NG);
   typename R4::T lw[NG];
@@ -441,34 +456,46 @@ __device__ __forceinline__ void tree_race_chunk(const TreeArgs<Elem>& a, int32_t
     merged = true;
   }
   const int32_t x0 = rc * kChunk;
-  for (int i = tid; i < kChunk / 32; i += kRaceThreads) bits[i] = 0u;
-  __syncthreads();
-  if (tid < 64 && lane < n && par == cur) {  // wavefront 0 holds the nodes
-    const int32_t x = tok - x0;
-    if (x >= 0 && x < kChunk) atomicOr(bits + (x >> 5), 1u << (x & 31));
+  if (!qrow) {  // the stop node's children leave the race (LDS bitmap of the chunk)
+    for (int i = tid; i < kChunk / 32; i += kRaceThreads) bits[i] = 0u;
+    __syncthreads();
+    if (tid < 64 && lane < n && par == cur) {  // wavefront 0 holds the nodes
+      const int32_t x = tok - x0;
+      if (x >= 0 && x < kChunk) atomicOr(bits + (x >> 5), 1u << (x & 31));
+    }
+    __syncthreads();
   }
-  __syncthreads();
   const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
   float best_key = 0.f;
   int32_t best_x = INT_MAX;
-  const float qz[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < NG; ++i) {
     const int32_t G = G0 + tid + i * kRaceThreads;
     if (G >= Gend) continue;
-    float l[4];
+    float l[4], qv[4] = {0.f, 0.f, 0.f, 0.f};
     if (G < Gfull) {
       R4::unpack(lw[i], l);
+      if (qrow) {
+        const float4 q4 = stream_load(reinterpret_cast<const float4*>(qrow) + G);
+        qv[0] = q4.x;
+        qv[1] = q4.y;
+        qv[2] = q4.z;
+        qv[3] = q4.w;
+      }
     } else {
-      float qd[4];
-      load_group_scalar(lrow, (const float*)nullptr, G, a.V, l, qd);
+      load_group_scalar(lrow, qrow, G, a.V, l, qv);
     }
-    const int32_t xl = 4 * G - x0;  // the group's offset in the chunk: bits 4 (G - G0) .. + 3
-    const uint32_t mb = bits[xl >> 5] >> (xl & 31);
+    if (qrow) {
+      race_group_m<kModeResampleQ, false>(l, qv, -1, cs, shift, inv_sum, -INFINITY, k0, k1, (uint32_t)d, (uint32_t)b,
+                                          G, best_key, best_x);
+    } else {
+      const int32_t xl = 4 * G - x0;  // the group's offset in the chunk: bits 4 (G - G0) .. + 3
+      const uint32_t mb = bits[xl >> 5] >> (xl & 31);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) l[k] = ((mb >> k) & 1u) ? -INFINITY : l[k];
-    race_group_m<kModeBonus, false>(l, qz, -1, cs, shift, inv_sum, -INFINITY, k0, k1, (uint32_t)d, (uint32_t)b, G,
-                                    best_key, best_x);
+      for (int k = 0; k < 4; ++k) l[k] = ((mb >> k) & 1u) ? -INFINITY : l[k];
+      race_group_m<kModeBonus, false>(l, qv, -1, cs, shift, inv_sum, -INFINITY, k0, k1, (uint32_t)d, (uint32_t)b, G,
+                                      best_key, best_x);
+    }
   }
   const unsigned long long win = block_reduce<kRaceThreads>(pack_key(best_key, best_x), lds_u, MaxOp());
   if (tid >= 64) return;
@@ -486,7 +513,7 @@ __device__ __forceinline__ void tree_race_chunk(const TreeArgs<Elem>& a, int32_t
     best = v > best ? v : best;
   }
   best = wave_max(best);
-  if (best == 0ull) {  // every token with mass is a child of the stop node: race over p
+  if (best == 0ull) {  // no token had weight (every token with mass a child, or p <= q everywhere): race over p
     float bk = 0.f;
     int32_t bx = INT_MAX;
     for (int32_t G = lane; G < Gend; G += 64) {

@@ -252,6 +252,7 @@ class TreeWorkload:
     seed: int
     num_nodes: List[int] = field(default_factory=list)
     max_depth: int = 0
+    draft_probs: Optional[torch.Tensor] = None  # [N + B, V] fp32 or None, rows aligned with logits
 
     @property
     def B(self) -> int:
@@ -272,7 +273,8 @@ class TreeWorkload:
     def to(self, device) -> "TreeWorkload":
         return TreeWorkload(self.name, self.logits.to(device), self.node_tokens.to(device),
                             self.node_parents.to(device), self.cu_num_nodes.to(device), self.temperature.to(device),
-                            self.seed, list(self.num_nodes), self.max_depth)
+                            self.seed, list(self.num_nodes), self.max_depth,
+                            None if self.draft_probs is None else self.draft_probs.to(device))
 
 
 def tree_shape(depth: int, branching: Sequence[int], max_nodes: int) -> List[int]:
@@ -294,11 +296,14 @@ def tree_shape(depth: int, branching: Sequence[int], max_nodes: int) -> List[int
 
 def make_tree(B: int, V: int, *, depth: int = 5, branching=(4, 2, 2, 1, 1), max_nodes: int = 64,
               dtype=torch.bfloat16, logit_std: float = 4.0, temperature=1.0, draft_noise: float = 1.0,
-              seed: int = 0, gen_seed: int = 2000, device="cpu", name: str = "tree") -> TreeWorkload:
+              seed: int = 0, gen_seed: int = 2000, device="cpu", name: str = "tree",
+              with_q: bool = False) -> TreeWorkload:
     """EAGLE-style draft trees: every request has the same shape (tree_shape);
     the children of a node are the top tokens of (that node's target row / T
     + N(0, draft_noise^2)), which is how a draft model that roughly agrees with
-    the target proposes them."""
+    the target proposes them.  with_q: also the draft distributions, the
+    softmax of that noisy row at every tree position (a childless node's row
+    gets noise of its own)."""
     device = torch.device(device)
     g = _gen(device, gen_seed)
     parents = tree_shape(depth, list(branching), max_nodes)
@@ -315,24 +320,35 @@ def make_tree(B: int, V: int, *, depth: int = 5, branching=(4, 2, 2, 1, 1), max_
     par = torch.tensor(parents, dtype=torch.int32)
     tokens = torch.empty(B, n, dtype=torch.int32)
     Tc = T.cpu()
+    q = torch.empty(R, V, dtype=torch.float32, device=device) if with_q else None
     for b in range(B):
         base = b * (n + 1)
+        Tb = float(Tc[b]) if float(Tc[b]) > 0 else 1.0
         for node_row in range(-1, n):
             kids = [i for i in range(n) if parents[i] == node_row]
             if not kids:
                 continue
-            Tb = float(Tc[b]) if float(Tc[b]) > 0 else 1.0
             row = widened[base + 1 + node_row] / Tb
             noisy = row + draft_noise * torch.randn(V, generator=g, device=device)
+            if q is not None:
+                q[base + 1 + node_row] = torch.softmax(noisy, 0)
             top = torch.topk(noisy, len(kids)).indices.cpu()
             for k, i in enumerate(kids):
                 tokens[b, i] = int(top[k])
+    if q is not None:  # childless nodes: the draft's row exists but proposed nothing
+        for b in range(B):
+            Tb = float(Tc[b]) if float(Tc[b]) > 0 else 1.0
+            for node_row in range(-1, n):
+                if node_row not in parents:
+                    r = b * (n + 1) + 1 + node_row
+                    noisy = widened[r] / Tb + draft_noise * torch.randn(V, generator=g, device=device)
+                    q[r] = torch.softmax(noisy, 0)
     cu = torch.arange(B + 1, dtype=torch.int32) * n
     depth_of = []
     for i, p_ in enumerate(parents):
         depth_of.append(0 if p_ < 0 else depth_of[p_] + 1)
     return TreeWorkload(name, logits.contiguous(), tokens.reshape(-1).to(device), par.repeat(B).to(device),
-                        cu.to(device), T.contiguous(), int(seed), [n] * B, (max(depth_of) + 1) if depth_of else 0)
+                        cu.to(device), T.contiguous(), int(seed), [n] * B, (max(depth_of) + 1) if depth_of else 0, q)
 
 
 def make_contexts(B: int, length, vocab: int = 151936, *, copy_prob: float = 0.5, span=(8, 48), seed: int = 0,

@@ -110,12 +110,12 @@ int main() {
   EXPECT(rs_verify_noalloc(nullptr, RS_BF16, nullptr, nullptr, I, F, 0, 0, 2, 100, 1, nullptr, nullptr, nullptr,
                            nullptr),
          RS_OK);
-  EXPECT(rs_verify_tree(P, RS_BF16, I, I, I, F, 2, 10, 65, 4, 100, 1, O, O, O, P, 1 << 30, nullptr),
+  EXPECT(rs_verify_tree(P, RS_BF16, nullptr, I, I, I, F, 2, 10, 65, 4, 100, 1, O, O, O, P, 1 << 30, nullptr),
          RS_ERR_INVALID_ARG);  // max_nodes > 64
-  EXPECT(rs_verify_tree(P, RS_BF16, I, I, I, F, 2, 10, 8, 9, 100, 1, O, O, O, P, 1 << 30, nullptr),
+  EXPECT(rs_verify_tree(P, RS_BF16, nullptr, I, I, I, F, 2, 10, 8, 9, 100, 1, O, O, O, P, 1 << 30, nullptr),
          RS_ERR_INVALID_ARG);  // max_depth > max_nodes
-  EXPECT(rs_verify_tree(P, RS_BF16, I, I, I, F, 2, 10, 8, 4, 100, 1, O, O, O, P, 16, nullptr), RS_ERR_WORKSPACE);
-  EXPECT(rs_verify_tree(nullptr, RS_BF16, nullptr, nullptr, I, F, 0, 0, 8, 4, 100, 1, nullptr, nullptr, nullptr,
+  EXPECT(rs_verify_tree(P, RS_BF16, nullptr, I, I, I, F, 2, 10, 8, 4, 100, 1, O, O, O, P, 16, nullptr), RS_ERR_WORKSPACE);
+  EXPECT(rs_verify_tree(nullptr, RS_BF16, nullptr, nullptr, nullptr, I, F, 0, 0, 8, 4, 100, 1, nullptr, nullptr, nullptr,
                         nullptr, 0, nullptr),
          RS_OK);
   EXPECT(rs_ngram_propose(I, I, 2, 10, 0, 3, 5, 100, O, O, O, P, 1 << 20, nullptr), RS_ERR_INVALID_ARG);

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert name in exported, name
         assert getattr(lib, name) is not None
-    assert lib.rs_abi_version() == 1
+    assert lib.rs_abi_version() == 2
 
 
 def test_status_codes_as_documented(lib):
@@ -264,7 +264,7 @@ def _call_tree(lib, **kw):
     a = dict(logits=DUMMY, dtype=1, tok=DUMMY, par=DUMMY, cu=DUMMY, T=DUMMY, B=2, N=10, max_nodes=8, max_depth=4,
              V=100, seed=0, out=DUMMY, path=DUMMY, nacc=DUMMY, ws=DUMMY, wsb=1 << 20, stream=None)
     a.update(kw)
-    return lib.rs_verify_tree(a["logits"], a["dtype"], a["tok"], a["par"], a["cu"], a["T"], a["B"], a["N"],
+    return lib.rs_verify_tree(a["logits"], a["dtype"], a.get("q"), a["tok"], a["par"], a["cu"], a["T"], a["B"], a["N"],
                               a["max_nodes"], a["max_depth"], a["V"], a["seed"], a["out"], a["path"], a["nacc"],
                               a["ws"], a["wsb"], a["stream"])
 
@@ -282,6 +282,7 @@ def _call_tree(lib, **kw):
     (dict(T=None), rs.RS_ERR_INVALID_ARG),
     (dict(logits=DUMMY + 1), rs.RS_ERR_UNSUPPORTED),
     (dict(par=DUMMY + 2), rs.RS_ERR_UNSUPPORTED),
+    (dict(q=DUMMY + 8), rs.RS_ERR_UNSUPPORTED),                 # draft rows must be 16-byte aligned
     (dict(ws=None), rs.RS_ERR_WORKSPACE),
     (dict(wsb=8), rs.RS_ERR_WORKSPACE),
 ])

@@ -30,7 +30,8 @@ def _say(msg):
 
 def _run(w):
     out, path, n = rs.verify_tree(w.logits, w.node_tokens, w.node_parents, w.cu_num_nodes, w.temperature,
-                                  seed=w.seed, max_nodes=w.max_nodes, max_depth=w.max_depth)
+                                  seed=w.seed, max_nodes=w.max_nodes, max_depth=w.max_depth,
+                                  draft_probs=w.draft_probs)
     torch.cuda.synchronize()
     return out.cpu().numpy(), path.cpu().numpy(), n.cpu().numpy()
 
@@ -38,7 +39,7 @@ def _run(w):
 def _oracle(w):
     c = w.to("cpu")
     return oracle.verify_tree(c.logits, c.node_tokens, c.node_parents, c.cu_num_nodes, c.temperature, c.seed,
-                              c.max_nodes, c.max_depth)
+                              c.max_nodes, c.max_depth, draft_probs=c.draft_probs)
 
 
 def _compare(w, g, o, max_flagged=1):
@@ -118,3 +119,68 @@ def test_tree_rerun_bit_identical():
     a, b = _run(w), _run(w)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
+
+
+Q_CASES = [
+    # name, B, V, dtype, depth, branching, max_nodes, temperature
+    ("q eagle bf16 V=151936 B=48", 48, 151936, torch.bfloat16, 5, (4, 2, 2, 1, 1), 64, ("uniform", 0.5, 1.2)),
+    ("q wide fp32 V=32001 mixed", 32, 32001, torch.float32, 3, (8, 3, 1), 64, [0.0, 0.8, 1.0, -1.0] * 8),
+    ("q tiny V=7 fp32", 50, 7, torch.float32, 3, (3, 2, 1), 20, 0.9),
+    ("q big vocab bf16 V=600001", 3, 600001, torch.bfloat16, 3, (3, 2, 1), 16, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", Q_CASES, ids=[c[0] for c in Q_CASES])
+def test_tree_parity_with_draft_probs(case):
+    """With draft distributions the extra token after a stop at a node with
+    children is the race over max(0, p - q) of that node's row; a childless
+    node's extra token still follows p."""
+    name, B, V, dt, depth, br, mn, T = case
+    w = W.make_tree(B, V, depth=depth, branching=br, max_nodes=mn, dtype=dt, temperature=T, seed=37,
+                    gen_seed=5000 + B, device="cuda", name=name, with_q=True)
+    _say(f"{name}: B={w.B} nodes/request={w.max_nodes} depth={w.max_depth}")
+    g = _run(w)
+    o = _oracle(w)
+    f = _compare(w, g, o)
+    _say(f"{name}: flagged {f}, mean accepted {o.num_accepted.mean():.3f}")
+
+
+def test_tree_q_on_siblings_equals_no_q():
+    """q_c = p_c on c's children's tokens and 0 elsewhere: max(0, p - q) is p
+    without the children, so the tokens equal those of the call without q."""
+    w = W.make_tree(24, 50000, depth=4, branching=(3, 2, 2, 1), max_nodes=40, dtype=torch.float32,
+                    temperature=("uniform", 0.6, 1.2), seed=23, gen_seed=77, device="cuda")
+    c = w.to("cpu")
+    cu, tok, par = c.cu_num_nodes.numpy(), c.node_tokens.numpy(), c.node_parents.numpy()
+    Tb = torch.where(c.temperature > 0, c.temperature, torch.ones_like(c.temperature))
+    rows_T = torch.repeat_interleave(Tb, torch.tensor([n + 1 for n in c.num_nodes]))
+    p = torch.softmax(c.logits.double() / rows_T.double()[:, None], 1)
+    q = torch.zeros_like(c.logits)
+    for b in range(w.B):
+        s, e = int(cu[b]), int(cu[b + 1])
+        for node in range(-1, e - s):
+            kids = torch.as_tensor(tok[s:e][par[s:e] == node], dtype=torch.long)
+            row = s + b + 1 + node
+            q[row, kids] = p[row, kids].float()
+    a = _run(w)
+    w.draft_probs = q.cuda()
+    g = _run(w)
+    o = _oracle(w)
+    _compare(w, g, o, max_flagged=2)
+    ok = ~o.near_tie
+    for x, y in zip(a, g):
+        np.testing.assert_array_equal(x[ok], y[ok])
+
+
+def test_tree_q_zero_residual_falls_back_to_p():
+    """q = 2p at every row: max(0, p - q) is zero wherever p > 0, so each stop
+    at a node with children races p (flagged by the oracle) and must still
+    match its candidates."""
+    w = W.make_tree(40, 4096, depth=3, branching=(2, 2, 1), max_nodes=16, dtype=torch.float32, temperature=1.0,
+                    seed=41, gen_seed=78, device="cuda")
+    c = w.to("cpu")
+    p = torch.softmax(c.logits.double(), 1)
+    w.draft_probs = (2 * p).float().cuda()
+    g = _run(w)
+    o = _oracle(w)
+    _compare(w, g, o, max_flagged=w.B)

@@ -29,7 +29,7 @@
 // a list of entries that its workgroups work through in order:
 //   a row entry (node x, step d): stream the row of x (the root: -1) in
 //     chunks of 8 vectors per thread into that row's partial statistics;
-//   a race entry (stop node, step d): race the stop row in 8192-token chunks
+//   a race entry (stop node, step d): race the stop row in 10240-token chunks
 //     (p without the stop node's children, or max(0, p - q) with the stop
 //     node's draft row q);
 //   an exit entry: the request is finished.
@@ -64,7 +64,7 @@ namespace rsv {
 constexpr int kTreeMaxNodes = 64;               // one wavefront lane per node
 constexpr int kTreeRows = kTreeMaxNodes + 1;    // the root row and one per node
 constexpr int kTreeEntries = kTreeRows + 2;     // every row at most once, the race, the exit
-constexpr int kTreeRaceTPT = 32;                // tokens per thread of a race chunk (8192 per chunk)
+constexpr int kTreeRaceTPT = 40;                // tokens per thread of a race chunk (10240 per chunk)
 constexpr int kTreeNV = 8;                      // 16-byte vectors per thread of a row chunk
 constexpr int kTreeSpec = 1;                    // children rows streamed before their parent is reached
 constexpr int32_t kTreeMaxK = 64;               // workgroups per request, at most
@@ -531,9 +531,11 @@ __device__ __forceinline__ void tree_race_chunk(const TreeArgs<Elem>& a, int32_t
 }
 
 // Workgroup k of request b = blockIdx / K: works through the request's
-// entries in order, claiming chunks of each until none is left.
+// entries in order, claiming chunks of each until none is left.  bf16 rows
+// fit four workgroups per CU (128 VGPRs): more workgroups per request, so a
+// 151936-token race (15 chunks) finishes in one round of claims.
 template <typename Elem, int NV>
-__global__ __launch_bounds__(kRowThreads) void tree_walk_kernel(TreeArgs<Elem> a) {
+__global__ __launch_bounds__(kRowThreads, sizeof(Elem) == 2 ? 4 : 3) void tree_walk_kernel(TreeArgs<Elem> a) {
   __shared__ unsigned long long s_e, s_w;
   __shared__ uint32_t s_c;
   const int32_t b = (int32_t)(blockIdx.x / a.K);

@@ -302,8 +302,7 @@ def make_tree(B: int, V: int, *, depth: int = 5, branching=(4, 2, 2, 1, 1), max_
     the children of a node are the top tokens of (that node's target row / T
     + N(0, draft_noise^2)), which is how a draft model that roughly agrees with
     the target proposes them.  with_q: also the draft distributions, the
-    softmax of that noisy row at every tree position (a childless node's row
-    gets noise of its own)."""
+    softmax of that noisy row at every tree position."""
     device = torch.device(device)
     g = _gen(device, gen_seed)
     parents = tree_shape(depth, list(branching), max_nodes)
@@ -318,31 +317,21 @@ def make_tree(B: int, V: int, *, depth: int = 5, branching=(4, 2, 2, 1, 1), max_
     else:
         T = torch.full((B,), float(temperature), dtype=torch.float32, device=device)
     par = torch.tensor(parents, dtype=torch.int32)
+    # one noisy row per tree position (a greedy request's rows at T = 1),
+    # drawn together; each node's children are the top tokens of its row
+    Trow = torch.where(T > 0, T, torch.ones_like(T)).repeat_interleave(n + 1)
+    noisy = widened / Trow[:, None] + draft_noise * torch.randn(R, V, generator=g, device=device)
+    nkids = [sum(1 for p_ in parents if p_ == node_row) for node_row in range(-1, n)]
+    kmax = max(nkids) if nkids else 0
     tokens = torch.empty(B, n, dtype=torch.int32)
-    Tc = T.cpu()
-    q = torch.empty(R, V, dtype=torch.float32, device=device) if with_q else None
-    for b in range(B):
-        base = b * (n + 1)
-        Tb = float(Tc[b]) if float(Tc[b]) > 0 else 1.0
+    if kmax > 0:
+        top = torch.topk(noisy, min(kmax, V), dim=1).indices.cpu().reshape(B, n + 1, -1)
         for node_row in range(-1, n):
             kids = [i for i in range(n) if parents[i] == node_row]
-            if not kids:
-                continue
-            row = widened[base + 1 + node_row] / Tb
-            noisy = row + draft_noise * torch.randn(V, generator=g, device=device)
-            if q is not None:
-                q[base + 1 + node_row] = torch.softmax(noisy, 0)
-            top = torch.topk(noisy, len(kids)).indices.cpu()
             for k, i in enumerate(kids):
-                tokens[b, i] = int(top[k])
-    if q is not None:  # childless nodes: the draft's row exists but proposed nothing
-        for b in range(B):
-            Tb = float(Tc[b]) if float(Tc[b]) > 0 else 1.0
-            for node_row in range(-1, n):
-                if node_row not in parents:
-                    r = b * (n + 1) + 1 + node_row
-                    noisy = widened[r] / Tb + draft_noise * torch.randn(V, generator=g, device=device)
-                    q[r] = torch.softmax(noisy, 0)
+                tokens[:, i] = top[:, 1 + node_row, k].to(torch.int32)
+    q = torch.softmax(noisy, dim=1) if with_q else None
+    del noisy
     cu = torch.arange(B + 1, dtype=torch.int32) * n
     depth_of = []
     for i, p_ in enumerate(parents):

@@ -32,13 +32,14 @@
 //   a race entry (stop node, step d): race the stop row in 10240-token chunks
 //     (p without the stop node's children, or max(0, p - q) with the stop
 //     node's draft row q);
-//   an exit entry: the request is finished.
+//   an exit entry: the request is finished;
+//   a no-op entry (a decided step's slot that holds nothing else).
 // A workgroup claims chunks of the entry it is at from that entry's counter
 // (the first claim is made while the entry may still be unwritten), so a row
 // is streamed by many workgroups at once and a workgroup that is deciding
 // holds no chunk back.  The init kernel writes the
 // first entries: the root row and the rows of the first kTreeSpec children of
-// the root.  Step d's decider appends the next ones: when it accepts node x,
+// the root.  Step d's decider writes the next ones: when it accepts node x,
 // the row of x if it was not streamed ahead and the rows of the first
 // kTreeSpec children of x (needed one step later); when a random walk stops,
 // the race entry; when the request is finished, the exit entry.
@@ -63,7 +64,9 @@ namespace rsv {
 
 constexpr int kTreeMaxNodes = 64;               // one wavefront lane per node
 constexpr int kTreeRows = kTreeMaxNodes + 1;    // the root row and one per node
-constexpr int kTreeEntries = kTreeRows + 2;     // every row at most once, the race, the exit
+// every row at most once, up to kTreeSpec slots per decided step (a no-op
+// when it holds nothing else), the race and the exit
+constexpr int kTreeEntries = 2 * kTreeRows + 2;
 constexpr int kTreeRaceTPT = 40;                // tokens per thread of a race chunk (10240 per chunk)
 constexpr int kTreeNV = 8;                      // 16-byte vectors per thread of a row chunk
 constexpr int kTreeSpec = 1;                    // children rows streamed before their parent is reached
@@ -74,9 +77,9 @@ constexpr uint32_t kChosen = 0x80000000u;       // row counter: the row's node w
 // update: the walk word (byte 0), the entry tail (byte 8), the entries (from
 // byte 128) and the entries' chunk claims (from byte 1024).  Each request's
 // words sit on lines of their own, away from other requests'.
-constexpr int kMailboxWords = 256;   // 8-byte words per mailbox
+constexpr int kMailboxWords = 512;   // 8-byte words per mailbox
 constexpr int kMailboxEntries = 16;  // first entry word
-constexpr int kMailboxClaims = 128;  // first word of the 32-bit claim counters
+constexpr int kMailboxClaims = kMailboxEntries + kTreeEntries;  // first word of the 32-bit claim counters
 static_assert(kMailboxEntries + kTreeEntries <= kMailboxClaims, "entries fit the mailbox");
 static_assert(kMailboxClaims + (kTreeEntries + 1) / 2 <= kMailboxWords, "claims fit the mailbox");
 
@@ -94,7 +97,7 @@ __device__ __forceinline__ uint32_t walk_status(unsigned long long w) { return (
 
 // Entry word: node + 1 (bits 0-7), step (8-15), chunks (16-39), kind
 // (40-41), bit 63 set (a zero word is an entry not yet written).
-constexpr uint32_t kEntryRow = 0, kEntryRace = 1, kEntryExit = 2;
+constexpr uint32_t kEntryRow = 0, kEntryRace = 1, kEntryExit = 2, kEntryNone = 3;
 __device__ __forceinline__ unsigned long long entry_word(uint32_t kind, int32_t node, int32_t d, int32_t chunks) {
   return (1ull << 63) | ((unsigned long long)kind << 40) | ((unsigned long long)(uint32_t)chunks << 16) |
          ((unsigned long long)(uint32_t)d << 8) | (uint32_t)(node + 1);
@@ -299,22 +302,36 @@ __device__ __forceinline__ void tree_finish(const TreeArgs<Elem>& a, int32_t b, 
 
 // Decisions of request b from step d on (wavefront 0 of the workgroup that
 // completed the pair for step d): merge the row's partials, choose the child
-// or stop, write the step's output and append the entries that come next;
-// while the next row is already complete, decide it too.
+// or stop, write the step's output and the entries that come next; while the
+// next row is already complete, decide it too.  Each step reserves
+// kTreeSpec entry slots with one atomic issued together with the row's loads:
+// they take the race or the exit when the walk stops, the rows of the chosen
+// node's first children (streamed one step ahead) when its own row was
+// streamed ahead, else its own row (the children's rows then take further
+// slots); a slot left over holds a no-op.  The chosen node's row counter is
+// read with those loads too: a row that is already complete needs no
+// handshake, since its last chunk has arrived without finding the chosen bit.
 template <typename Elem>
 __device__ __forceinline__ void tree_decide(const TreeArgs<Elem>& a, int32_t b, int32_t d, int32_t cur, int32_t s,
                                             int32_t n, float T, int32_t tok, int32_t par) {
+  static_assert(kTreeSpec >= 1, "a step's slots hold at least the race or the exit");
   const int lane = threadIdx.x & 63;
   const bool greedy = !(T > 0.f);
   const float cs = greedy ? 0.f : scale_of(T);
   int32_t* ob = a.out + (int64_t)b * (a.max_depth + 1);
   int32_t* pb = a.path + (int64_t)b * a.max_depth;
+  unsigned long long* E = entries_of(a, b);
+  uint32_t* rc = a.count + (int64_t)b * kTreeRows + 1;  // row counter of node x: rc[x]
   for (;;) {
     const int64_t row = (int64_t)s + b + 1 + cur;
     const Elem* prow = a.logits + row * (int64_t)a.V;
     const bool child = lane < n && par == cur;
-    // the children's logits and the partials are loaded together
+    // the children's logits and row counters, the partials and the slots are requested together
     const float lt = (!greedy && child) ? to_f32(prow[tok]) : -INFINITY;
+    const uint32_t early = child ? __hip_atomic_load(rc + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    uint32_t base = 0u;
+    if (lane == 0)
+      base = __hip_atomic_fetch_add(tail_of(a, b), (uint32_t)kTreeSpec, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     float shift = -INFINITY;
     double S = 0.0;
     int32_t amax = -1, next = -1;
@@ -343,45 +360,57 @@ __device__ __forceinline__ void tree_decide(const TreeArgs<Elem>& a, int32_t b, 
         }
       }
     }
+    base = (uint32_t)lane_i32((int32_t)base, 0);
     if (next < 0) {  // stop at step d
-      if (greedy) {
-        if (lane == 0) {
+      if (lane == 0) {
+        if (greedy) {
           ob[d] = amax;
           a.nacc[b] = d;
+          store_coherent(walk_of(a, b), walk_word((uint32_t)d, cur, kWalkDone));
+        } else {  // the extra token: the race over p without the stop node's children
+          store_coherent(walk_of(a, b), walk_word((uint32_t)d, cur, kStopped));
         }
-        tree_finish(a, b, d, cur);
-        return;
       }
-      // the extra token: the race over p without the stop node's children
-      if (lane == 0) store_coherent(walk_of(a, b), walk_word((uint32_t)d, cur, kStopped));
-      tree_append(a, b, entry_word(kEntryRace, cur, d, a.race_chunks));
+      if (lane < kTreeSpec && base + lane < (uint32_t)kTreeEntries)
+        store_coherent(E + base + lane, lane > 0  ? entry_word(kEntryNone, -1, d, 0)
+                                        : greedy ? entry_word(kEntryExit, -1, 0, 0)
+                                                 : entry_word(kEntryRace, cur, d, a.race_chunks));
       return;
     }
     // descend: the accepted node is emitted, and step d + 1 decides among its children
     const int32_t ntok = lane_i32(tok, next);
-    const int32_t rank = child_rank(par, n, next);
-    const unsigned long long spec = __ballot(lane < n && par == next);  // next's children, the first few streamed now
-    const int32_t nspec = min(__popcll(spec), kTreeSpec);
-    const int32_t own = rank >= kTreeSpec ? 1 : 0;  // next's row was not streamed ahead
-    const int32_t nent = own + nspec;
-    uint32_t base = 0u, old = 0u;
+    const bool own = child_rank(par, n, next) >= kTreeSpec;  // next's row was not streamed ahead
+    const unsigned long long nkids = __ballot(lane < n && par == next);
+    const int32_t nspec = min(__popcll(nkids), kTreeSpec);  // next's first children, streamed one step ahead
     if (lane == 0) {
       ob[d] = ntok;
       pb[d] = next;
       store_coherent(walk_of(a, b), walk_word((uint32_t)d + 1, next, kWalking));
-      if (nent > 0) base = __hip_atomic_fetch_add(tail_of(a, b), (uint32_t)nent, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (lane == 1)  // next is reached: its row's last chunk, or this decider, decides step d + 1
-      old = __hip_atomic_fetch_or(a.count + (int64_t)b * kTreeRows + next + 1, kChosen, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-    base = (uint32_t)lane_i32((int32_t)base, 0);
-    old = (uint32_t)lane_i32((int32_t)old, 1);
-    if (lane < nent && base + lane < (uint32_t)kTreeEntries) {
-      const int32_t x = lane < own ? next : nth_bit(spec, lane - own);
-      store_coherent(entries_of(a, b) + base + lane,
-                     entry_word(kEntryRow, x, x == next ? d + 1 : d + 2, a.nsplit));
+    // the reserved slots: next's row (if not streamed ahead), then its first children's rows, no-ops after
+    const int32_t nent = (own ? 1 : 0) + nspec;
+    if (lane < kTreeSpec && base + lane < (uint32_t)kTreeEntries) {
+      const int32_t x = lane < nent ? (own && lane == 0 ? next : nth_bit(nkids, lane - (own ? 1 : 0))) : -1;
+      store_coherent(E + base + lane, x < 0 ? entry_word(kEntryNone, -1, d, 0)
+                                            : entry_word(kEntryRow, x, x == next ? d + 1 : d + 2, a.nsplit));
     }
-    if (old != (uint32_t)a.nsplit) return;  // the row is still streaming
+    if (nent > kTreeSpec) {  // the rest (next's own row took a slot)
+      uint32_t b2 = 0u;
+      if (lane == 0)
+        b2 = __hip_atomic_fetch_add(tail_of(a, b), (uint32_t)(nent - kTreeSpec), __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+      b2 = (uint32_t)lane_i32((int32_t)b2, 0);
+      if (lane >= kTreeSpec && lane < nent && b2 + (lane - kTreeSpec) < (uint32_t)kTreeEntries)
+        store_coherent(E + b2 + (lane - kTreeSpec), entry_word(kEntryRow, nth_bit(nkids, lane - 1), d + 2, a.nsplit));
+    }
+    const bool complete = !own && (uint32_t)lane_i32((int32_t)early, next) == (uint32_t)a.nsplit;
+    if (!complete) {  // next is reached: its row's last chunk, or this decider, decides step d + 1
+      uint32_t old = 0u;
+      if (lane == 0)
+        old = __hip_atomic_fetch_or(rc + next, kChosen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      old = (uint32_t)lane_i32((int32_t)old, 0);
+      if (old != (uint32_t)a.nsplit) return;  // the row is still streaming
+    }
     ++d;
     cur = next;
   }
@@ -571,6 +600,7 @@ __global__ __launch_bounds__(kRowThreads, sizeof(Elem) == 2 ? 4 : 3) void tree_w
     uint32_t c = s_c;
     __syncthreads();  // s_e, s_w and s_c are rewritten below
     if (!ent || entry_kind(ent) == kEntryExit) return;
+    if (entry_kind(ent) == kEntryNone) continue;
     const uint32_t chunks = (uint32_t)entry_chunks(ent);
     const int32_t x = entry_node(ent), d = entry_step(ent);
     const bool race = entry_kind(ent) == kEntryRace;

@@ -115,6 +115,8 @@ int main() {
   EXPECT(rs_verify_tree(P, RS_BF16, nullptr, I, I, I, F, 2, 10, 8, 9, 100, 1, O, O, O, P, 1 << 30, nullptr),
          RS_ERR_INVALID_ARG);  // max_depth > max_nodes
   EXPECT(rs_verify_tree(P, RS_BF16, nullptr, I, I, I, F, 2, 10, 8, 4, 100, 1, O, O, O, P, 16, nullptr), RS_ERR_WORKSPACE);
+  EXPECT(rs_verify_tree(P, RS_BF16, F + 2, I, I, I, F, 2, 10, 8, 4, 100, 1, O, O, O, P, 1 << 30, nullptr),
+         RS_ERR_UNSUPPORTED);  // draft rows not 16-byte aligned
   EXPECT(rs_verify_tree(nullptr, RS_BF16, nullptr, nullptr, nullptr, I, F, 0, 0, 8, 4, 100, 1, nullptr, nullptr, nullptr,
                         nullptr, 0, nullptr),
          RS_OK);

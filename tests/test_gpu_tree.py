@@ -184,3 +184,23 @@ def test_tree_q_zero_residual_falls_back_to_p():
     g = _run(w)
     o = _oracle(w)
     _compare(w, g, o, max_flagged=w.B)
+
+
+def test_tree_draft_probs_argument_checks():
+    """draft_probs must be fp32 with N + B rows of V on the logits' device, and
+    16-byte aligned (a view one element in fails in the library)."""
+    w = W.make_tree(4, 1000, depth=2, branching=(2, 1), max_nodes=8, dtype=torch.float32, seed=3, gen_seed=71,
+                    device="cuda", with_q=True)
+    args = (w.logits, w.node_tokens, w.node_parents, w.cu_num_nodes, w.temperature)
+    kw = dict(seed=w.seed, max_nodes=w.max_nodes, max_depth=w.max_depth)
+    with pytest.raises(ValueError):
+        rs.verify_tree(*args, draft_probs=w.draft_probs[:-1], **kw)
+    with pytest.raises(TypeError):
+        rs.verify_tree(*args, draft_probs=w.draft_probs.double(), **kw)
+    flat = torch.empty(w.draft_probs.numel() + 1, dtype=torch.float32, device="cuda")
+    flat[1:] = w.draft_probs.reshape(-1)
+    with pytest.raises(RuntimeError):
+        rs.verify_tree(*args, draft_probs=flat[1:].view_as(w.draft_probs), **kw)
+    out, path, n = rs.verify_tree(*args, draft_probs=w.draft_probs, **kw)
+    torch.cuda.synchronize()
+    assert (n.cpu() >= 0).all()

@@ -46,8 +46,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_codes_as_documented(lib):
     """The status codes the header declares (RS_ERR_WORKSPACE = 3 and
-    RS_ERR_HIP = 4, a departure from the survey's sketch recorded in the
-    design notes), their strings and the binding's constants."""
+    RS_ERR_HIP = 4: a workspace error is reported apart from a launch
+    failure), their strings and the binding's constants."""
     src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
     enum = dict((k, int(v)) for k, v in re.findall(r"\b(RS_(?:OK|ERR_[A-Z_]+))\s*=\s*(\d+)", src))
     assert enum == {"RS_OK": 0, "RS_ERR_INVALID_ARG": 1, "RS_ERR_UNSUPPORTED": 2, "RS_ERR_WORKSPACE": 3,

@@ -273,3 +273,30 @@ def test_q_ignored_at_a_childless_node():
     assert leaf.mean() > 0.9
     assert _chi2(np.bincount(r.tokens[leaf, 1], minlength=V), p_leaf) > PVAL
     assert (r.tokens[leaf, 1] == np.argmax(p_leaf)).mean() > 0.5 * p_leaf.max()
+
+
+def test_tree_workload_recipe():
+    """The EAGLE-style tree inputs: every request has the breadth-first shape,
+    children are distinct top tokens of their parent's noisy row, and the
+    draft rows are that row's softmax (one per tree position, summing to 1)."""
+    import torch
+    w = W.make_tree(5, 400, depth=3, branching=(3, 2, 1), max_nodes=20, dtype=torch.float32, temperature=0.8,
+                    draft_noise=0.5, seed=1, gen_seed=9, with_q=True)
+    n = w.max_nodes
+    par = w.node_parents.numpy().reshape(w.B, n)
+    tok = w.node_tokens.numpy().reshape(w.B, n)
+    assert (par == par[0]).all() and w.max_depth == 3
+    q = w.draft_probs.numpy().astype(np.float64)
+    assert q.shape == (w.N + w.B, 400) and (q >= 0).all()
+    np.testing.assert_allclose(q.sum(1), 1.0, rtol=1e-5)
+    for b in range(w.B):
+        for node_row in range(-1, n):
+            kids = [i for i in range(n) if par[b, i] == node_row]
+            if not kids:
+                continue
+            row = b * (n + 1) + 1 + node_row
+            ks = tok[b, kids]
+            assert len(set(ks.tolist())) == len(kids)
+            # the children are the draft row's most likely tokens, in order
+            order = np.argsort(-q[row], kind="stable")[:len(kids)]
+            assert ks.tolist() == order.tolist()

@@ -69,6 +69,12 @@ CASES = [
                                            28, std=0.3)),
     ("fp32 q flat V=100000", lambda: _case("fp32 q flat V=100000", [2] * 12, 100000, torch.float32, "noise", 1.5,
                                            29, std=0.5)),
+    # more than 4096 segment maxima per row (V > 2^19 bf16): thresholds come
+    # from the selection over the whole row, with no bound from the maxima
+    ("bf16 q V=600001", lambda: _case("bf16 q V=600001", [2, 0, 3, 1] * 3, 600001, torch.bfloat16, "noise",
+                                      ("uniform", 0.5, 1.3), 30)),
+    ("fp32 onehot V=300007", lambda: _case("fp32 onehot V=300007", [3, 1, 2] * 3, 300007, torch.float32, "none",
+                                           [1.0, 0.0, 0.8] * 3, 31)),
 ]
 MAX_FLAGGED = {"bf16 q flat V=151936": 4, "fp32 q flat V=100000": 4}
 

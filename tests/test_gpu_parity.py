@@ -307,6 +307,30 @@ def test_invalid_metadata_rows():
     assert o.num_accepted[1] == -1
 
 
+@pytest.mark.parametrize("path", [0, 1, 2, 3])
+def test_invalid_requests_every_path(path):
+    """Requests made invalid by a draft id V at position 1, a draft id -7 at
+    position 0 or a last offset beyond D get n = -1 and a -1 row on every
+    path, at a vocabulary of three row chunks per row, and the valid requests
+    beside them, one with K = 0, match the oracle."""
+    g0 = torch.Generator().manual_seed(29)
+    V, ks = 70001, [3, 2, 0, 2, 3]
+    D, B = sum(ks), len(ks)
+    rows = (torch.randn(D + B, V, generator=g0) * 3).to(torch.bfloat16)
+    q = torch.softmax(rows[:D].float() + 0.5 * torch.randn(D, V, generator=g0), 1)
+    drafts = torch.randint(0, V, (D,), generator=g0, dtype=torch.int32)
+    drafts[3 + 1] = V   # request 1, position 1
+    drafts[5] = -7      # request 3, position 0
+    w = _custom(rows, q, drafts, ks, [1.0, 1.0, 0.7, 1.0, 1.0], seed=5)
+    w.cu_num_draft_tokens = torch.tensor([0, 3, 5, 5, 7, 11], dtype=torch.int32, device="cuda")  # request 4: e > D
+    _say(f"invalid requests, V={V}, path {path}")
+    g, o = run_gpu(w, path=path), run_oracle(w)
+    bad = [1, 3, 4]
+    assert (o.num_accepted[bad] == -1).all() and (o.num_accepted[[0, 2]] >= 0).all()
+    assert (g.num_accepted[bad] == -1).all() and (g.tokens[bad] == -1).all()
+    compare(g, o, w)
+
+
 # ------------------------------------------- 10^6 requests: parity + marginal = p
 def test_million_requests_parity_and_marginal():
     V, B, T = 8, 1_000_000, 1.0

@@ -70,10 +70,12 @@ def test_random_parity_sweep(seed):
         compare_p(g, o, w)
 
 
-def _random_trees(rng):
+def _random_trees(rng, with_q=False):
     """Ragged random trees (node i's parent uniform over the earlier nodes and
     the prefix), children's tokens mostly near the top of their parent's row,
-    sometimes random or repeated; mixed greedy / random temperatures."""
+    sometimes random or repeated; mixed greedy / random temperatures.  with_q:
+    also draft distributions, one per tree position, each the softmax of its
+    row plus N(0, 1) noise."""
     V = int(rng.choice([7, 1000, 32000, 151936]))
     B = int(rng.integers(1, 40 if V > 32000 else 100))
     max_nodes = int(rng.choice([8, 20, 64]))
@@ -103,28 +105,35 @@ def _random_trees(rng):
         tokens += tk
         rows.append(lg)
     logits = torch.cat(rows).to(dtype).contiguous().cuda()
+    q = None
+    if with_q:
+        lq = torch.cat(rows)
+        noise = torch.from_numpy(rng.standard_normal(lq.shape).astype(np.float32))
+        q = torch.softmax(lq + noise, dim=1).contiguous().cuda()
     cu = torch.tensor(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
     T = torch.tensor(rng.choice([0.0, 0.6, 1.0, 1.4], size=B).astype(np.float32)).cuda()
     w = W.TreeWorkload("random trees", logits, torch.tensor(tokens, dtype=torch.int32).cuda(),
                        torch.tensor(parents, dtype=torch.int32).cuda(), cu, T, int(rng.integers(0, 2**40)),
-                       [int(c) for c in counts], depth_max)
-    return w, max_nodes, f"B={B} V={V} max_nodes={max_nodes} {str(dtype).split('.')[-1]} depth {depth_max}"
+                       [int(c) for c in counts], depth_max, draft_probs=q)
+    return w, max_nodes, (f"B={B} V={V} max_nodes={max_nodes} {str(dtype).split('.')[-1]} depth {depth_max}"
+                          + (" with q" if with_q else ""))
 
 
-@pytest.mark.parametrize("seed", [11, 12])
-def test_random_tree_sweep(seed):
+@pytest.mark.parametrize("seed,with_q", [(11, False), (12, False), (13, True), (14, True)])
+def test_random_tree_sweep(seed, with_q):
     import oracle
     rng = np.random.default_rng(seed)
     for case in range(12):
-        w, max_nodes, desc = _random_trees(rng)
+        w, max_nodes, desc = _random_trees(rng, with_q)
         print(f"[gpu-case] tree sweep {seed} case {case}: {desc}", flush=True)
         max_depth = max(w.max_depth, 1)
         out, path, n = rs.verify_tree(w.logits, w.node_tokens, w.node_parents, w.cu_num_nodes, w.temperature,
-                                      seed=w.seed, max_nodes=max_nodes, max_depth=max_depth)
+                                      seed=w.seed, max_nodes=max_nodes, max_depth=max_depth,
+                                      draft_probs=w.draft_probs)
         torch.cuda.synchronize()
         c = w.to("cpu")
         o = oracle.verify_tree(c.logits, c.node_tokens, c.node_parents, c.cu_num_nodes, c.temperature, c.seed,
-                               max_nodes, max_depth)
+                               max_nodes, max_depth, draft_probs=c.draft_probs)
         compare_tree(out.cpu().numpy(), path.cpu().numpy(), n.cpu().numpy(), o, w, max_depth)
 
 

@@ -109,6 +109,7 @@ __global__ __launch_bounds__(kRowThreads) void phase_kernel(
     is_row = n_row > both;
   }
   if (is_row) {
+    __builtin_amdgcn_s_setprio(1);  // row waves ahead of race waves on a SIMD, as in the stream kernel
     const int32_t c = t % nsplit;
     const int32_t rest = t / nsplit;
     const int32_t j = j_begin + rest % j_count;

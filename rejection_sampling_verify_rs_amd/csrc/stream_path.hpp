@@ -235,6 +235,11 @@ template <typename Elem, int NV, int TPT>
 __device__ __forceinline__ void stream_row_task(const StreamArgs<Elem>& a, int32_t j, int32_t b, int32_t c,
                                                 int32_t* s_word) {
   const int tid = threadIdx.x;
+  // Row waves get issue priority over race waves on the same SIMD (a wave's
+  // arbitration priority only): their loads go out sooner while the races'
+  // arithmetic fills the gaps.  The call measured ~1 us faster at B=256 K=8
+  // V=151936.  A row task that races instead drops back to the default.
+  __builtin_amdgcn_s_setprio(1);
   const int32_t s = a.cu[b], e = a.cu[b + 1];
   const float T = a.greedy_all ? 0.f : a.temperature[b];
   // The workgroup agrees on one reading of the request's state.
@@ -249,6 +254,7 @@ __device__ __forceinline__ void stream_row_task(const StreamArgs<Elem>& a, int32
   const int32_t K = e - s;  // in range: the init kernel validated the request
   if (j > K) return;
   if (st >= 2 && ((st - 2) & (kStateReady - 1)) < j) {  // decided before position j: row not needed
+    __builtin_amdgcn_s_setprio(0);
     if (st >= kStateReady) (void)stream_race_claim<Elem, TPT>(a, b, s_word);
     return;
   }

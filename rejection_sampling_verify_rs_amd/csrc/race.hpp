@@ -93,7 +93,7 @@ __device__ __forceinline__ void load_group_scalar(const Elem* __restrict__ lrow,
 // Groups G0 + tid + i * kRaceThreads (i < TPT / 4) of one row.  FULL: every
 // group lies below Gfull (vector-loadable), so loads and arithmetic run
 // unguarded and the loads can be waited on one at a time.
-template <typename Elem, int TPT, int MODE, bool FILT, bool FULL>
+template <typename Elem, int TPT, int MODE, bool FILT, bool FULL, bool PRIO>
 __device__ __forceinline__ void race_span(const Elem* __restrict__ lrow, const float* __restrict__ qrow, int32_t V,
                                           int32_t G0, int32_t Gfull, int32_t Gend, int32_t exclude, float cs,
                                           float shift, float inv_sum, float tau, uint32_t k0, uint32_t k1, uint32_t j,
@@ -104,7 +104,9 @@ __device__ __forceinline__ void race_span(const Elem* __restrict__ lrow, const f
   const int tid = threadIdx.x;
   typename R4::T lw[NG];
   float4 qw[NG];
-  // Issue every load of this thread before any arithmetic.
+  // Issue every load of this thread before any arithmetic (PRIO: at raised
+  // issue priority, back to the default for the arithmetic).
+  if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int i = 0; i < NG; ++i) {
     const int32_t G = G0 + tid + i * kRaceThreads;
@@ -113,6 +115,7 @@ __device__ __forceinline__ void race_span(const Elem* __restrict__ lrow, const f
       if (kQ) qw[i] = stream_load(reinterpret_cast<const float4*>(qrow) + G);
     }
   }
+  if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
   for (int i = 0; i < NG; ++i) {
     const int32_t G = G0 + tid + i * kRaceThreads;
@@ -134,7 +137,7 @@ __device__ __forceinline__ void race_span(const Elem* __restrict__ lrow, const f
   }
 }
 
-template <typename Elem, int TPT, int MODE, bool FILT>
+template <typename Elem, int TPT, int MODE, bool FILT, bool PRIO>
 __device__ __forceinline__ unsigned long long race_chunk_m(const Elem* __restrict__ logits,
                                                            const float* __restrict__ q, int32_t V, uint64_t seed,
                                                            const ReqRecord& rec, int32_t b, int32_t c) {
@@ -152,11 +155,11 @@ __device__ __forceinline__ unsigned long long race_chunk_m(const Elem* __restric
   float best_key = 0.f;
   int32_t best_x = INT_MAX;
   if (G0 + kRaceThreads * NG <= Gfull)
-    race_span<Elem, TPT, MODE, FILT, true>(lrow, qrow, V, G0, Gfull, Gend, rec.exclude, rec.c, rec.shift,
+    race_span<Elem, TPT, MODE, FILT, true, PRIO>(lrow, qrow, V, G0, Gfull, Gend, rec.exclude, rec.c, rec.shift,
                                            rec.inv_sum, rec.tau, k0, k1, (uint32_t)rec.n, (uint32_t)b, best_key,
                                            best_x);
   else
-    race_span<Elem, TPT, MODE, FILT, false>(lrow, qrow, V, G0, Gfull, Gend, rec.exclude, rec.c, rec.shift,
+    race_span<Elem, TPT, MODE, FILT, false, PRIO>(lrow, qrow, V, G0, Gfull, Gend, rec.exclude, rec.c, rec.shift,
                                             rec.inv_sum, rec.tau, k0, k1, (uint32_t)rec.n, (uint32_t)b, best_key,
                                             best_x);
   return block_reduce<kRaceThreads>(pack_key(best_key, best_x), lds_u, MaxOp());
@@ -165,21 +168,21 @@ __device__ __forceinline__ unsigned long long race_chunk_m(const Elem* __restric
 // One workgroup races chunk c (kRaceThreads * TPT tokens) of request b's
 // sampled row described by `rec` and returns the packed best of the chunk
 // (0 = no positive key) in every thread.
-template <typename Elem, int TPT>
+template <typename Elem, int TPT, bool PRIO = false>
 __device__ __forceinline__ unsigned long long race_chunk(const Elem* __restrict__ logits, const float* __restrict__ q,
                                                          int32_t V, uint64_t seed, const ReqRecord& rec, int32_t b,
                                                          int32_t c) {
   if (rec.tau > -INFINITY) {  // filtered target distribution (top-k / top-p)
     if (rec.mode == kModeResampleQ)
-      return race_chunk_m<Elem, TPT, kModeResampleQ, true>(logits, q, V, seed, rec, b, c);
+      return race_chunk_m<Elem, TPT, kModeResampleQ, true, PRIO>(logits, q, V, seed, rec, b, c);
     if (rec.mode == kModeResampleOneHot)
-      return race_chunk_m<Elem, TPT, kModeResampleOneHot, true>(logits, q, V, seed, rec, b, c);
-    return race_chunk_m<Elem, TPT, kModeBonus, true>(logits, q, V, seed, rec, b, c);
+      return race_chunk_m<Elem, TPT, kModeResampleOneHot, true, PRIO>(logits, q, V, seed, rec, b, c);
+    return race_chunk_m<Elem, TPT, kModeBonus, true, PRIO>(logits, q, V, seed, rec, b, c);
   }
-  if (rec.mode == kModeResampleQ) return race_chunk_m<Elem, TPT, kModeResampleQ, false>(logits, q, V, seed, rec, b, c);
+  if (rec.mode == kModeResampleQ) return race_chunk_m<Elem, TPT, kModeResampleQ, false, PRIO>(logits, q, V, seed, rec, b, c);
   if (rec.mode == kModeResampleOneHot)
-    return race_chunk_m<Elem, TPT, kModeResampleOneHot, false>(logits, q, V, seed, rec, b, c);
-  return race_chunk_m<Elem, TPT, kModeBonus, false>(logits, q, V, seed, rec, b, c);
+    return race_chunk_m<Elem, TPT, kModeResampleOneHot, false, PRIO>(logits, q, V, seed, rec, b, c);
+  return race_chunk_m<Elem, TPT, kModeBonus, false, PRIO>(logits, q, V, seed, rec, b, c);
 }
 
 // Output of one request, by wavefront 0 of the workgroup that raced its last

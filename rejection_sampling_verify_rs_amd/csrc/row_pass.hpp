@@ -244,7 +244,7 @@ __device__ __forceinline__ RowStats row_stats(const Elem* __restrict__ prow, int
 // tmax (NULL: not wanted) receives every thread's own maximum of the chunk
 // (kRowThreads floats, -inf for a thread with no element): the top-k / top-p
 // selection uses them to bound its threshold.
-template <typename Elem, int NV, bool COH = false>
+template <typename Elem, int NV, bool COH = false, bool PRIO_DROP = false>
 __device__ __forceinline__ void chunk_task(const Elem* __restrict__ logits, const float* __restrict__ q, int64_t row,
                                            float T, int32_t V, int32_t nsplit, int32_t c, int32_t xstar,
                                            int64_t slot, RowPartial* __restrict__ row_partials,
@@ -280,6 +280,9 @@ __device__ __forceinline__ void chunk_task(const Elem* __restrict__ logits, cons
       if (v < nvec) data[i] = pv[v];
     }
   }
+  // PRIO_DROP: the caller raised this wave's issue priority for its loads;
+  // the arithmetic runs at the default.
+  if constexpr (PRIO_DROP) __builtin_amdgcn_s_setprio(0);
   float extra = -INFINITY;
   int extra_idx = INT_MAX;
   if (c == 0) {

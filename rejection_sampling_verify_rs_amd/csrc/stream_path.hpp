@@ -214,7 +214,7 @@ __device__ __forceinline__ bool stream_race_claim(const StreamArgs<Elem>& a, int
   const int32_t c = *s_word;  // every thread reads it before race_chunk's barriers
   if (c >= a.race_chunks) return false;
   const ReqRecord rec = load_record(a.records + b);
-  const unsigned long long packed = race_chunk<Elem, TPT>(a.logits, a.q, a.V, a.seed, rec, b, c);
+  const unsigned long long packed = race_chunk<Elem, TPT, true>(a.logits, a.q, a.V, a.seed, rec, b, c);
   if (tid < 64) {  // wavefront 0 reports the chunk winner
     int last = 0;
     if (tid == 0) {
@@ -235,10 +235,13 @@ template <typename Elem, int NV, int TPT>
 __device__ __forceinline__ void stream_row_task(const StreamArgs<Elem>& a, int32_t j, int32_t b, int32_t c,
                                                 int32_t* s_word) {
   const int tid = threadIdx.x;
-  // Row waves get issue priority over race waves on the same SIMD (a wave's
-  // arbitration priority only): their loads go out sooner while the races'
-  // arithmetic fills the gaps.  The call measured ~1 us faster at B=256 K=8
-  // V=151936.  A row task that races instead drops back to the default.
+  // Waves issue their loads at raised priority (a wave's arbitration priority
+  // among the waves of its SIMD) and do their arithmetic at the default, so
+  // the loads of every task go out as early as possible while the arithmetic
+  // of others fills the gaps: row tasks here until their loads are issued
+  // (chunk_task drops it), race chunks around their loads.  At B=256 K=8
+  // V=151936 the call went from 121.3 to 120.2 us with raised row tasks and
+  // to ~117 us with the drop after the loads.
   __builtin_amdgcn_s_setprio(1);
   const int32_t s = a.cu[b], e = a.cu[b + 1];
   const float T = a.greedy_all ? 0.f : a.temperature[b];
@@ -260,7 +263,7 @@ __device__ __forceinline__ void stream_row_task(const StreamArgs<Elem>& a, int32
   }
   const int32_t xstar = (c == 0 && j < K && T > 0.f) ? a.draft[s + j] : -1;
   const int64_t row = (int64_t)s + b + j;
-  chunk_task<Elem, NV, true>(a.logits, a.q, row, T, a.V, a.nsplit, c, xstar, (int64_t)s + j,
+  chunk_task<Elem, NV, true, true>(a.logits, a.q, row, T, a.V, a.nsplit, c, xstar, (int64_t)s + j,
                              a.partials + row * a.nsplit, a.gath);
   if (tid >= 64) return;  // wavefront 0 reports the chunk
   int last = 0;

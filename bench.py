@@ -521,9 +521,14 @@ def main():
         # min_n 3, max_n 8, k 5 (the pages' example settings)
         ctx, ccu = W.make_contexts(64, 4096, w0.V, seed=3, device=dev)
         holder = {}
+        nb = int(ccu.numel()) - 1
+        ng_out = (torch.empty(nb * 5, dtype=torch.int32, device=dev), torch.empty(nb, dtype=torch.int32, device=dev),
+                  torch.empty(nb + 1, dtype=torch.int32, device=dev))
+        ng_ws = torch.empty(nb * 5, dtype=torch.int32, device=dev)
 
-        def ngram_call(k):
-            holder["r"] = rs.ngram_propose(ctx, ccu, min_n=3, max_n=8, k=5, stream=stream)
+        def ngram_call(k):  # outputs and workspace allocated once, as a serving loop would
+            holder["r"] = rs.ngram_propose(ctx, ccu, min_n=3, max_n=8, k=5, out=ng_out, workspace=ng_ws,
+                                           stream=stream)
 
         st = timed_region(ngram_call, args.steps, args.warmup, stream)
         variants["ngram_B64_ctx4096"] = {**st, "context_tokens_per_s": ctx.numel() / (st["ms_per_step"] / 1e3),

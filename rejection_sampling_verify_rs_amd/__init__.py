@@ -426,10 +426,14 @@ def verify_tree(target_logits: torch.Tensor, node_tokens: torch.Tensor, node_par
 
 
 def ngram_propose(context_token_ids: torch.Tensor, cu_context: torch.Tensor, *, min_n: int, max_n: int, k: int,
-                  max_model_len: int = 1 << 62, stream: Optional[torch.cuda.Stream] = None):
+                  max_model_len: int = 1 << 62, out: Optional[tuple] = None, workspace: Optional[torch.Tensor] = None,
+                  stream: Optional[torch.cuda.Stream] = None):
     """n-gram drafts (rs_ngram_propose).  Returns (draft_token_ids packed [B * k],
     num_draft_tokens [B], cu_num_draft_tokens [B + 1]); the first
-    cu_num_draft_tokens[-1] drafts are valid."""
+    cu_num_draft_tokens[-1] drafts are valid.  out: optional preallocated
+    (draft_token_ids, num_draft_tokens, cu_num_draft_tokens) int32 tensors of
+    at least B * k, B and B + 1 elements; workspace: optional int32 scratch of
+    at least B * k elements (with both, a call allocates nothing)."""
     lib = load_library()
     if not isinstance(context_token_ids, torch.Tensor) or context_token_ids.device.type != "cuda":
         raise ValueError("context_token_ids must be a CUDA (HIP) tensor")
@@ -439,10 +443,28 @@ def ngram_propose(context_token_ids: torch.Tensor, cu_context: torch.Tensor, *, 
     B = int(cu_context.numel()) - 1
     if B < 0:
         raise ValueError("cu_context needs B + 1 entries")
-    drafts = torch.empty(max(B * k, 1), dtype=torch.int32, device=dev)
-    num = torch.empty(max(B, 1), dtype=torch.int32, device=dev)[:B]
-    cu = torch.zeros(B + 1, dtype=torch.int32, device=dev)
-    ws = torch.empty(max(B * k, 1), dtype=torch.int32, device=dev)
+    if out is None:
+        drafts = torch.empty(max(B * k, 1), dtype=torch.int32, device=dev)
+        num = torch.empty(max(B, 1), dtype=torch.int32, device=dev)[:B]
+        # the pack kernel writes every prefix sum; with no request nothing runs, so cu = [0] here
+        cu = torch.zeros(1, dtype=torch.int32, device=dev) if B == 0 else torch.empty(B + 1, dtype=torch.int32,
+                                                                                          device=dev)
+    else:
+        drafts, num, cu = out
+        for t, name, need in ((drafts, "draft_token_ids", B * k), (num, "num_draft_tokens", B),
+                              (cu, "cu_num_draft_tokens", B + 1)):
+            _dev_tensor(t, name, torch.int32, dev)
+            if t.numel() < need:
+                raise ValueError(f"{name} needs at least {need} elements")
+        if B == 0:
+            cu[:1].zero_()
+    if workspace is None:
+        ws = torch.empty(max(B * k, 1), dtype=torch.int32, device=dev)
+    else:
+        ws = workspace
+        _dev_tensor(ws, "workspace", torch.int32, dev)
+        if ws.numel() < B * k:
+            raise ValueError(f"workspace needs at least {B * k} int32 elements")
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     T = int(context_token_ids.numel())
@@ -450,4 +472,4 @@ def ngram_propose(context_token_ids: torch.Tensor, cu_context: torch.Tensor, *, 
                                 int(min_n), int(max_n), int(k), int(max_model_len), drafts.data_ptr(),
                                 num.data_ptr() if B > 0 else None, cu.data_ptr(), ws.data_ptr(),
                                 ws.numel() * 4, ctypes.c_void_p(stream.cuda_stream)))
-    return drafts[: B * k], num, cu
+    return drafts[: B * k], num[:B], cu[: B + 1]

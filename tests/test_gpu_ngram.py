@@ -73,3 +73,34 @@ def test_proposer_then_verify():
     o = oracle.verify(logits.cpu(), None, drafts.cpu(), c.cpu(), T.cpu(), 21, 6)
     w = W.Workload("ngram drafts", logits, None, drafts, c, T, 21, n.cpu().tolist())
     compare(GpuResult(out.cpu().numpy(), acc.cpu().numpy()), o, w)
+
+
+def test_preallocated_outputs_and_workspace():
+    """Outputs and workspace passed in (poisoned first) give the allocating
+    call's results, on a call and on a smaller one after it; with no request
+    cu_num_draft_tokens is [0]; short buffers are refused."""
+    dev = torch.device("cuda")
+    out = (torch.full((64 * 8,), -7, dtype=torch.int32, device=dev), torch.full((64,), -7, dtype=torch.int32, device=dev),
+           torch.full((65,), -7, dtype=torch.int32, device=dev))
+    ws = torch.full((64 * 8,), -7, dtype=torch.int32, device=dev)
+    for B, L in ((64, 1500), (23, (0, 700))):
+        flat, cu = W.make_contexts(B, L, 500, seed=B + 1, device="cuda")
+        print(f"[gpu-case] ngram preallocated B={B}", flush=True)
+        d0, n0, c0 = rs.ngram_propose(flat, cu, min_n=2, max_n=6, k=8)
+        d1, n1, c1 = rs.ngram_propose(flat, cu, min_n=2, max_n=6, k=8, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        assert d1.data_ptr() == out[0].data_ptr() and c1.numel() == B + 1 and n1.numel() == B
+        np.testing.assert_array_equal(n1.cpu().numpy(), n0.cpu().numpy())
+        np.testing.assert_array_equal(c1.cpu().numpy(), c0.cpu().numpy())
+        D = int(c0[-1])
+        np.testing.assert_array_equal(d1[:D].cpu().numpy(), d0[:D].cpu().numpy())
+    empty_cu = torch.zeros(1, dtype=torch.int32, device=dev)
+    _, n2, c2 = rs.ngram_propose(torch.zeros(0, dtype=torch.int32, device=dev), empty_cu, min_n=1, max_n=2, k=3,
+                                 out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert n2.numel() == 0 and c2.cpu().tolist() == [0]
+    flat, cu = W.make_contexts(64, 100, 50, seed=9, device="cuda")
+    with pytest.raises(ValueError):
+        rs.ngram_propose(flat, cu, min_n=1, max_n=2, k=9, out=out, workspace=ws)
+    with pytest.raises(ValueError):
+        rs.ngram_propose(flat, cu, min_n=1, max_n=2, k=8, out=out, workspace=ws[:10])

@@ -667,16 +667,16 @@ struct TreeLayout {
   size_t off_mail, off_count, off_race_count, off_partials, off_cand, total;
 };
 
-// Row chunks of a row: 16-byte vectors per row over vectors per chunk.
+// Row chunks of a row: 16-byte vectors per row over vectors per chunk (nv per thread).
 template <typename Elem>
-static int32_t tree_nsplit(int32_t vocab) {
+static int32_t tree_nsplit(int32_t vocab, int nv) {
   const int64_t nvec = vocab / Vec<Elem>::W;
-  return (int32_t)std::max<int64_t>(1, (nvec + kTreeNV * kRowThreads - 1) / (kTreeNV * kRowThreads));
+  return (int32_t)std::max<int64_t>(1, (nvec + nv * kRowThreads - 1) / (nv * kRowThreads));
 }
 
 static TreeLayout tree_layout(int32_t batch, int32_t vocab) {
   TreeLayout t;
-  t.nsplit_max = tree_nsplit<float>(vocab);  // fp32 rows have the most chunks
+  t.nsplit_max = tree_nsplit<float>(vocab, kTreeNV);  // fp32 rows at the smaller chunks have the most
   constexpr int32_t kChunk = kRaceThreads * kTreeRaceTPT;
   t.race_chunks = (vocab + kChunk - 1) / kChunk;
   const size_t B = (size_t)batch;
@@ -690,15 +690,15 @@ static TreeLayout tree_layout(int32_t batch, int32_t vocab) {
 }
 
 // Workgroups the device holds at once for the walk kernel (queried once per
-// device and element type).
-template <typename Elem>
+// device, element type and chunk size).
+template <typename Elem, int NV>
 static int64_t tree_resident() {
   static int64_t cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
   if (cached[dev] == 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, tree_walk_kernel<Elem, kTreeNV>, kRowThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, tree_walk_kernel<Elem, NV>, kRowThreads, 0) !=
             hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu < 1 ||
         cus < 1)
@@ -728,12 +728,22 @@ static rs_status launch_tree(const void* logits, const float* q, const int32_t* 
   a.max_nodes = max_nodes;
   a.max_depth = max_depth;
   a.V = V;
-  a.nsplit = tree_nsplit<Elem>(V);
   a.race_chunks = t.race_chunks;
   // K workgroups per request, enough to fill the device once (any of a
   // request's workgroups can take any of its chunks, so none waits on one
   // that is not resident).
-  a.K = (int32_t)std::max<int64_t>(1, std::min<int64_t>(kTreeMaxK, tree_resident<Elem>() / B));
+  auto per_request = [&](int64_t resident) {
+    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(kTreeMaxK, resident / B));
+  };
+  a.K = per_request(tree_resident<Elem, kTreeNV>());
+  bool wide = false;
+  if constexpr (sizeof(Elem) == 2) {
+    if (a.K <= kTreeWideK) {
+      wide = true;
+      a.K = per_request(tree_resident<Elem, kTreeNVWide>());
+    }
+  }
+  a.nsplit = tree_nsplit<Elem>(V, wide ? kTreeNVWide : kTreeNV);
   a.out = out;
   a.path = path;
   a.nacc = nacc;
@@ -744,6 +754,12 @@ static rs_status launch_tree(const void* logits, const float* q, const int32_t* 
   a.cand = reinterpret_cast<unsigned long long*>(w + t.off_cand);
   tree_init_kernel<Elem><<<(unsigned)B, kRowThreads, 0, stream>>>(a);
   if (hipGetLastError() != hipSuccess) return RS_ERR_HIP;
+  if constexpr (sizeof(Elem) == 2) {
+    if (wide) {
+      tree_walk_kernel<Elem, kTreeNVWide><<<(unsigned)((int64_t)B * a.K), kRowThreads, 0, stream>>>(a);
+      return hipGetLastError() == hipSuccess ? RS_OK : RS_ERR_HIP;
+    }
+  }
   tree_walk_kernel<Elem, kTreeNV><<<(unsigned)((int64_t)B * a.K), kRowThreads, 0, stream>>>(a);
   return hipGetLastError() == hipSuccess ? RS_OK : RS_ERR_HIP;
 }

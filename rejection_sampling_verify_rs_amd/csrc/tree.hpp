@@ -69,6 +69,12 @@ constexpr int kTreeRows = kTreeMaxNodes + 1;    // the root row and one per node
 constexpr int kTreeEntries = 2 * kTreeRows + 2;
 constexpr int kTreeRaceTPT = 40;                // tokens per thread of a race chunk (10240 per chunk)
 constexpr int kTreeNV = 8;                      // 16-byte vectors per thread of a row chunk
+// bf16 rows when a request has at most kTreeWideK workgroups (B >= ~86 on a
+// 256-CU device): fewer, larger chunks per row, so a row takes fewer rounds of
+// claims on those workgroups (B=128: 86 -> 81 us, B=256: 151 -> 139 us; B=48:
+// 55 against 58 us with the smaller chunks)
+constexpr int kTreeNVWide = 12;
+constexpr int32_t kTreeWideK = 12;
 constexpr int kTreeSpec = 1;                    // children rows streamed before their parent is reached
 constexpr int32_t kTreeMaxK = 64;               // workgroups per request, at most
 constexpr int32_t kTreePollLimit = 1 << 18;     // polls before a workgroup stops waiting for an entry

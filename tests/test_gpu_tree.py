@@ -53,6 +53,8 @@ CASES = [
     # name, B, V, dtype, depth, branching, max_nodes, temperature
     ("eagle bf16 V=151936 B=64", 64, 151936, torch.bfloat16, 5, (4, 2, 2, 1, 1), 64, ("uniform", 0.5, 1.2)),
     ("eagle bf16 greedy V=151936", 32, 151936, torch.bfloat16, 5, (4, 2, 2, 1, 1), 64, 0.0),
+    # at most 12 workgroups per request: the walk streams rows in 12-vector chunks
+    ("eagle bf16 V=151936 B=128", 128, 151936, torch.bfloat16, 5, (4, 2, 2, 1, 1), 64, ("uniform", 0.5, 1.2)),
     ("wide fp32 V=32000 mixed", 40, 32000, torch.float32, 3, (8, 3, 1), 64, [0.0, 0.8, 1.0, -1.0] * 10),
     ("deep bf16 V=50000", 24, 50000, torch.bfloat16, 8, (2, 2, 2, 1, 1, 1, 1, 1), 48, 1.0),
     ("tiny V=7 fp32", 50, 7, torch.float32, 3, (3, 2, 1), 20, 0.9),
@@ -124,6 +126,7 @@ def test_tree_rerun_bit_identical():
 Q_CASES = [
     # name, B, V, dtype, depth, branching, max_nodes, temperature
     ("q eagle bf16 V=151936 B=48", 48, 151936, torch.bfloat16, 5, (4, 2, 2, 1, 1), 64, ("uniform", 0.5, 1.2)),
+    ("q eagle bf16 V=151936 B=96", 96, 151936, torch.bfloat16, 5, (4, 2, 2, 1, 1), 64, ("uniform", 0.5, 1.2)),
     ("q wide fp32 V=32001 mixed", 32, 32001, torch.float32, 3, (8, 3, 1), 64, [0.0, 0.8, 1.0, -1.0] * 8),
     ("q tiny V=7 fp32", 50, 7, torch.float32, 3, (3, 2, 1), 20, 0.9),
     ("q big vocab bf16 V=600001", 3, 600001, torch.bfloat16, 3, (3, 2, 1), 16, 1.0),
